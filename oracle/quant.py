@@ -1,0 +1,125 @@
+"""The three group quantizers of the FP8 linear-layer flow (oracle; test infrastructure only).
+
+Source: Resumen Técnico: Jet-RL (gist.science), section "Esquema de
+Cuantización" -- activations are quantized in 1x128 groups, weights in 128x128
+blocks, and the WGrad operands in 1x128 / 128x1 groups; "Arquitectura
+Central" -- master weights are bf16 and one quantization flow serves rollout
+and training.
+
+One group G of bf16 values is quantized as follows (every step in IEEE
+binary32, round-to-nearest-even, no flush-to-zero):
+
+    x_j  = float32(G_j)                    exact widening of bf16
+    amax = max_j |x_j|                     exact
+    s    = 1.0                 if amax == 0   (an all-zero group; reading: keeps
+                                               the rule uniform and decodes to 0)
+         = fl32(amax / 448)    otherwise      (one float32 division)
+    q_j  = E4M3_RNE( fl32(x_j / s) )          (one float32 division per element,
+                                               then the codec in e4m3.encode)
+
+A group is 128 consecutive elements of a row (1x128), a 128x128 tile
+(128x128), or 128 consecutive rows of one column (128x1). Shapes must be
+multiples of 128 along every grouped dimension.
+
+Inputs are bf16 bit patterns (uint16 arrays); outputs are E4M3 bytes (uint8)
+and float32 scales.
+"""
+
+import numpy as np
+
+from .e4m3 import bf16_bits_to_f32, encode
+
+GROUP = 128
+FP8_MAX = np.float32(448.0)
+
+
+def quantize_group(values_f32):
+    """Quantize one group (any shape) of float32 values that came from bf16.
+
+    Returns (codes uint8 of the same shape, scale as np.float32).
+    """
+    x = np.asarray(values_f32, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
+    if amax == 0:
+        s = np.float32(1.0)
+    else:
+        s = np.float32(amax / FP8_MAX)           # float32 / float32 -> float32
+    q = encode(np.float32(x / s))                # float32 division, then RNE
+    return q, s
+
+
+def _grouped_scales_and_codes(groups):
+    """Apply quantize_group to every row of a [G, n] array (vectorised form).
+
+    Identical to calling quantize_group on each row: the amax is per row, the
+    scale is one float32 division per row, the quotient one float32 division
+    per element.
+    """
+    g = np.asarray(groups, dtype=np.float32)
+    amax = np.max(np.abs(g), axis=1)
+    s = np.where(amax == 0, np.float32(1.0),
+                 (amax / FP8_MAX).astype(np.float32)).astype(np.float32)
+    q = encode((g / s[:, None]).astype(np.float32))
+    return q, s
+
+
+def quantize_act_1x128(x_bits):
+    """1x128 per-token group quantization of a bf16 [M, K] activation.
+
+    Source: "Esquema de Cuantización", activations bullet (1x128 per group);
+    the same quantizer serves dY before DGrad (backward GEMMs in FP8).
+
+    Returns xq uint8 [M, K] and xs float32 [M, K/128], where xs[m, g] is the
+    scale of x[m, 128g : 128g + 128].
+    """
+    x = bf16_bits_to_f32(x_bits)
+    M, K = x.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    Kg = K // GROUP
+    q, s = _grouped_scales_and_codes(x.reshape(M * Kg, GROUP))
+    return q.reshape(M, K), s.reshape(M, Kg)
+
+
+def quantize_weight_128x128(w_bits):
+    """128x128 per-block quantization of a bf16 [N, K] weight.
+
+    Source: "Esquema de Cuantización", weights bullet (128x128 per block);
+    "Arquitectura Central", bf16 master weights re-quantized for each use.
+
+    Returns wq uint8 [N, K], ws float32 [N/128, K/128] (ws[i, j] is the scale
+    of w[128i : 128i + 128, 128j : 128j + 128]) and wq_t = wq transposed
+    ([K, N]), the operand layout DGrad reads. A 128x128 block has the same
+    amax transposed, so wq_t is exactly the byte transpose of wq.
+    """
+    w = bf16_bits_to_f32(w_bits)
+    N, K = w.shape
+    if N % GROUP or K % GROUP:
+        raise ValueError("N and K must be multiples of 128")
+    Nb, Kb = N // GROUP, K // GROUP
+    blocks = w.reshape(Nb, GROUP, Kb, GROUP).transpose(0, 2, 1, 3)
+    q, s = _grouped_scales_and_codes(blocks.reshape(Nb * Kb, GROUP * GROUP))
+    wq = q.reshape(Nb, Kb, GROUP, GROUP).transpose(0, 2, 1, 3).reshape(N, K)
+    ws = s.reshape(Nb, Kb)
+    return wq, ws, np.ascontiguousarray(wq.T)
+
+
+def transpose_quantize_128x1(x_bits):
+    """128x1 group quantization of a bf16 [M, C] tensor, written transposed.
+
+    Source: "Esquema de Cuantización", backward bullets: WGrad runs in FP8
+    with 1x128 / 128x1 operand groups, and saved activations are kept in FP8.
+    Each group is 128 consecutive tokens of one channel, i.e. it runs along
+    the token dimension, which is WGrad's contraction dimension.
+
+    Returns xq_t uint8 [C, M] and xs_t float32 [C, M/128]; xs_t[c, b] is the
+    scale of x[128b : 128b + 128, c], and xq_t[c, m] is the code of x[m, c].
+    """
+    x = bf16_bits_to_f32(x_bits)
+    M, C = x.shape
+    if M % GROUP:
+        raise ValueError("M must be a multiple of 128")
+    Mb = M // GROUP
+    xt = np.ascontiguousarray(x.T)                      # [C, M]
+    q, s = _grouped_scales_and_codes(xt.reshape(C * Mb, GROUP))
+    return q.reshape(C, M), s.reshape(C, Mb)

@@ -1,0 +1,200 @@
+"""Pins of the oracle's fp64 GEMMs, bf16 rounding and tolerance check.
+
+* exact integer/rational triple loops on tiny shapes with random codes and
+  random (non power-of-two) scales, for all three GEMMs;
+* one-hot and identity operands through the quantizers;
+* lossless operands (tests of the exact-GEMM construction used on the GPU);
+* bf16 rounding against exact rational rounding and torch's float32 cast;
+* the tolerance rule at and around its boundary.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_block_scaled_quantize_amd.inputs import exact_operand, f32_to_bf16_bits, tensor_streams
+from oracle import e4m3, gemm, quant
+from tests._exact import e4m3_values, rn_bf16
+
+# Code -> integer multiple of 2^-9, from the enumerated grid (not from decode()).
+_UNITS = {}
+for _c, _v in e4m3_values():
+    _UNITS[_c] = int(_v * 512)
+    _UNITS[_c | 0x80] = -int(_v * 512)
+
+
+def _rand_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x7E                  # no NaN codes
+    return c
+
+
+def _rand_scales(rng, shape):
+    return (rng.uniform(0.5, 2.0, size=shape) * np.exp2(rng.integers(-12, 4, size=shape))).astype(np.float32)
+
+
+def _exact_dot(a_codes, a_scales, b_codes, b_scales):
+    """sum over 128-blocks of (integer dot of codes) * 2^-18 * sa * sb, exactly."""
+    total = Fraction(0)
+    for kb in range(len(a_scales)):
+        acc = 0
+        for k in range(128 * kb, 128 * kb + 128):
+            acc += _UNITS[int(a_codes[k])] * _UNITS[int(b_codes[k])]
+        total += Fraction(acc, 2 ** 18) * Fraction(float(a_scales[kb])) * Fraction(float(b_scales[kb]))
+    return total
+
+
+def _check_close(oracle_val, exact, a_codes, a_scales, b_codes, b_scales):
+    mag = sum(abs(_UNITS[int(x)] * _UNITS[int(y)]) for x, y in zip(a_codes, b_codes))
+    bound = 1e-12 * (float(mag) / 2 ** 18 * float(np.max(a_scales)) * float(np.max(b_scales)) + 1e-300)
+    assert abs(Fraction(float(oracle_val)) - exact) <= Fraction(bound)
+
+
+def test_fwd_exact_triple_loop():
+    rng = np.random.default_rng(21)
+    M, N, K = 3, 256, 384
+    xq, xs = _rand_codes(rng, (M, K)), _rand_scales(rng, (M, K // 128))
+    wq, ws = _rand_codes(rng, (N, K)), _rand_scales(rng, (N // 128, K // 128))
+    y = gemm.gemm_fwd(xq, xs, wq, ws)
+    for m in range(M):
+        for n in list(range(0, 256, 37)) + [127, 128, 255]:
+            ex = _exact_dot(xq[m], xs[m], wq[n], ws[n // 128])
+            _check_close(y[m, n], ex, xq[m], xs[m], wq[n], ws[n // 128])
+
+
+def test_dgrad_exact_triple_loop():
+    rng = np.random.default_rng(22)
+    M, N, K = 3, 384, 256
+    dyq, dys = _rand_codes(rng, (M, N)), _rand_scales(rng, (M, N // 128))
+    wq, ws = _rand_codes(rng, (N, K)), _rand_scales(rng, (N // 128, K // 128))
+    dx = gemm.gemm_dgrad(dyq, dys, wq, ws)
+    for m in range(M):
+        for k in list(range(0, 256, 41)) + [127, 128, 255]:
+            col_codes = wq[:, k]
+            col_scales = ws[:, k // 128]
+            ex = _exact_dot(dyq[m], dys[m], col_codes, col_scales)
+            _check_close(dx[m, k], ex, dyq[m], dys[m], col_codes, col_scales)
+
+
+def test_wgrad_exact_triple_loop():
+    rng = np.random.default_rng(23)
+    M, N, K = 384, 3, 256
+    dyq_t, dys_t = _rand_codes(rng, (N, M)), _rand_scales(rng, (N, M // 128))
+    xq_t, xs_t = _rand_codes(rng, (K, M)), _rand_scales(rng, (K, M // 128))
+    dw = gemm.gemm_wgrad(dyq_t, dys_t, xq_t, xs_t)
+    for n in range(N):
+        for k in list(range(0, 256, 43)) + [127, 128, 255]:
+            ex = _exact_dot(dyq_t[n], dys_t[n], xq_t[k], xs_t[k])
+            _check_close(dw[n, k], ex, dyq_t[n], dys_t[n], xq_t[k], xs_t[k])
+
+
+def test_identity_weight_through_quantizer():
+    """W = 448 * I quantizes to exact 448 on the diagonal (scale 1) and zero blocks elsewhere."""
+    N = K = 256
+    w = np.zeros((N, K), np.uint16)
+    w[np.arange(N), np.arange(N)] = f32_to_bf16_bits(np.array([448.0], np.float32))[0]
+    wq, ws, wq_t = quant.quantize_weight_128x128(w)
+    assert np.all(ws == 1.0)
+    (g,) = tensor_streams(31, 1)
+    x = f32_to_bf16_bits(g.standard_normal((128, K)).astype(np.float32))
+    xq, xs = quant.quantize_act_1x128(x)
+    y = gemm.gemm_fwd(xq, xs, wq, ws)
+    assert np.array_equal(y, 448.0 * gemm.dequant_rows(xq, xs))
+    # DGrad with the (symmetric) identity weight returns 448 * dy_hat.
+    dx = gemm.gemm_dgrad(xq, xs, wq, ws)
+    assert np.array_equal(dx, 448.0 * gemm.dequant_rows(xq, xs))
+
+
+def test_one_hot_rows_select_weight_rows():
+    rng = np.random.default_rng(5)
+    N, K = 256, 256
+    wq, ws = _rand_codes(rng, (N, K)), _rand_scales(rng, (2, 2))
+    xq = np.zeros((4, K), np.uint8)
+    cols = [0, 129, 200, 255]
+    for m, k in enumerate(cols):
+        xq[m, k] = 0x38                             # 1.0
+    xs = np.ones((4, 2), np.float32)
+    y = gemm.gemm_fwd(xq, xs, wq, ws)
+    w_hat = gemm.dequant_blocks(wq, ws)
+    for m, k in enumerate(cols):
+        assert np.array_equal(y[m], w_hat[:, k])
+
+
+def test_wgrad_identity_tokens():
+    """dY^T X with X = I over tokens returns dY^T itself (dequantized)."""
+    rng = np.random.default_rng(9)
+    M, N = 256, 128
+    dyq_t, dys_t = _rand_codes(rng, (N, M)), _rand_scales(rng, (N, 2))
+    xq_t = np.zeros((M, M), np.uint8)
+    xq_t[np.arange(M), np.arange(M)] = 0x38
+    xs_t = np.ones((M, 2), np.float32)
+    dw = gemm.gemm_wgrad(dyq_t, dys_t, xq_t, xs_t)
+    assert np.array_equal(dw, gemm.dequant_rows(dyq_t, dys_t))
+
+
+def test_exact_operands_are_lossless_and_gemm_exact():
+    g1, g2 = tensor_streams(41, 2)
+    M, N, K = 256, 384, 512
+    x = exact_operand(g1, M, K, np.array([[-2] * 4, [1] * 4]))
+    w = exact_operand(g2, N, K, np.array([[-7] * 4, [-5] * 4, [-6] * 4]))
+    xq, xs = quant.quantize_act_1x128(x)
+    wq, ws, _ = quant.quantize_weight_128x128(w)
+    assert set(np.unique(xs)) == {np.float32(0.25), np.float32(2.0)}
+    assert np.array_equal(gemm.dequant_rows(xq, xs), e4m3.bf16_bits_to_f32(x).astype(np.float64))
+    assert np.array_equal(gemm.dequant_blocks(wq, ws), e4m3.bf16_bits_to_f32(w).astype(np.float64))
+    y = gemm.gemm_fwd(xq, xs, wq, ws)
+    # Exact: the same product in integer units.
+    xi = np.rint(e4m3.bf16_bits_to_f32(x).astype(np.float64) * 2.0 ** 4).astype(np.int64)
+    wi = np.rint(e4m3.bf16_bits_to_f32(w).astype(np.float64) * 2.0 ** 13).astype(np.int64)
+    assert np.array_equal(xi.astype(np.float64) / 2.0 ** 4, e4m3.bf16_bits_to_f32(x).astype(np.float64))
+    assert np.array_equal(wi.astype(np.float64) / 2.0 ** 13, e4m3.bf16_bits_to_f32(w).astype(np.float64))
+    yi = xi @ wi.T
+    assert np.array_equal(y, yi.astype(np.float64) / 2.0 ** 17)
+    assert np.max(np.abs(yi)) < 2 ** 53
+
+
+# ------------------------------------------------------------------ bf16 --
+
+def test_bf16_rne_against_exact_rounding():
+    rng = np.random.default_rng(77)
+    vals = list(rng.standard_normal(300) * np.exp2(rng.integers(-140, 40, 300)))
+    # exact midpoints between bf16 neighbours, and midpoints nudged by far less than a float32 ulp
+    for b in rng.integers(0x0001, 0x7F00, 100):
+        lo = float(e4m3.bf16_bits_to_f32(np.array([b], np.uint16))[0])
+        hi = float(e4m3.bf16_bits_to_f32(np.array([b + 1], np.uint16))[0])
+        mid = (lo + hi) / 2
+        vals += [mid, -mid, mid + (hi - lo) * 2.0 ** -30, mid - (hi - lo) * 2.0 ** -30]
+    vals = np.array(vals)
+    got = gemm.bf16_rne(vals)
+    for v, g in zip(vals, got):
+        want = rn_bf16(Fraction(float(v)))
+        assert Fraction(float(gemm.bf16_bits_to_f64(np.array([g]))[0])) == want, v
+
+
+def test_bf16_rne_matches_torch_on_float32():
+    rng = np.random.default_rng(78)
+    v = (rng.standard_normal(100000) * np.exp2(rng.integers(-130, 100, 100000))).astype(np.float32)
+    got = gemm.bf16_rne(v.astype(np.float64))
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------- tolerance --
+
+def test_tolerance_boundary():
+    ref = np.array([256.0, -1.0, 0.0, 4.0])
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    bound = 2.0 ** -7 * np.abs(ref) + 1e-3 * rms
+    inside = gemm.bf16_rne(ref + 0.9 * bound)
+    ok, info = gemm.within_tolerance(inside, ref)
+    assert ok, info
+    # 256 + 2 (next bf16 above 256 is 258) exceeds 2^-7 * 256 + 1e-3 * rms = 2.128? no: 2 < 2.128
+    out = gemm.bf16_rne(np.array([258.0, -1.0, 0.0, 4.0]))
+    assert gemm.within_tolerance(out, ref)[0]
+    out = gemm.bf16_rne(np.array([260.0, -1.0, 0.0, 4.0]))   # error 4 > 2.128
+    ok, info = gemm.within_tolerance(out, ref)
+    assert not ok and info["violations"] == 1
+    out = gemm.bf16_rne(np.array([256.0, -1.0, 0.25, 4.0]))  # error 0.25 > 1e-3 * rms
+    assert not gemm.within_tolerance(out, ref)[0]
