@@ -1,0 +1,204 @@
+"""MI355X (gfx950) FP8 block-scaled linear-layer library: Python binding.
+
+A thin ctypes layer over the C ABI of ``libfp8bsq.so`` (declared in
+``include/fp8bsq.h``). It only marshals arguments: it takes torch tensors that
+live in HIP device memory, checks dtype/shape/contiguity, allocates outputs
+with ``torch.empty`` when the caller does not pass them, and hands raw device
+pointers plus the current HIP stream to the library. Every step of the
+computation runs in the library's HIP kernels; there is no fallback. If the
+library is missing, every call raises.
+
+Entry points (same names as the C ABI):
+    quantize_act_1x128(x)             -> (xq [M,K] uint8, xs [M,K/128] float32)
+    quantize_weight_128x128(w, transposed=True)
+                                      -> (wq [N,K], ws [N/128,K/128], wq_t [K,N] or None)
+    transpose_quantize_128x1(x)       -> (xq_t [C,M], xs_t [C,M/128])
+    fp8_gemm_fwd(xq, xs, wq, ws)      -> y  [M,N] bf16      (Y = X W^T)
+    fp8_gemm_dgrad(dyq, dys, wq_t, ws) -> dx [M,K] bf16     (dX = dY W)
+    fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t) -> dw [N,K] bf16 (dW = dY^T X)
+    cast_f32_e4m3(v)                  -> E4M3 bytes of fp32 values
+E4M3 codes are returned as uint8 tensors (OCP E4M3 bytes); view them as
+``torch.float8_e4m3fn`` if needed. Every function accepts preallocated
+outputs through keyword arguments (``out=...``) and never synchronizes.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8bsq.so")
+
+_lib = None
+
+
+class Fp8bsqError(RuntimeError):
+    """A C-ABI call returned a non-zero status."""
+
+    def __init__(self, fn, status, message):
+        super().__init__(f"{fn}: status {status}: {message}")
+        self.status = status
+
+
+def library_path():
+    return LIB_PATH
+
+
+def load_library():
+    """Load libfp8bsq.so (after torch, so its HIP runtime is the one in use)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- loads torch's libamdhip64 first; the library binds to it by soname
+
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m fp8_block_scaled_quantize_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sigs = {
+        "fp8bsq_strerror": ([i32], ctypes.c_char_p),
+        "fp8bsq_abi_version": ([], i32),
+        "quantize_act_1x128": ([vp, i64, i64, vp, vp, vp], i32),
+        "quantize_weight_128x128": ([vp, i64, i64, vp, vp, vp, vp], i32),
+        "transpose_quantize_128x1": ([vp, i64, i64, vp, vp, vp], i32),
+        "fp8_gemm_fwd": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
+        "fp8_gemm_dgrad": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
+        "fp8_gemm_wgrad": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
+        "fp8bsq_cast_f32_e4m3": ([vp, vp, i64, vp], i32),
+    }
+    for name, (args, res) in sigs.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def strerror(status):
+    return load_library().fp8bsq_strerror(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise Fp8bsqError(fn, status, strerror(status))
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(t, name, dtype, shape):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be in GPU memory, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _out(t, name, dtype, shape, like):
+    import torch
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    return _need(t, name, dtype, shape)
+
+
+def quantize_act_1x128(x, xq=None, xs=None):
+    import torch
+    M, K = x.shape
+    _need(x, "x", torch.bfloat16, (M, K))
+    xq = _out(xq, "xq", torch.uint8, (M, K), x)
+    xs = _out(xs, "xs", torch.float32, (M, K // 128), x)
+    _check("quantize_act_1x128", load_library().quantize_act_1x128(
+        _ptr(x), M, K, _ptr(xq), _ptr(xs), _stream(x)))
+    return xq, xs
+
+
+def quantize_weight_128x128(w, transposed=True, wq=None, ws=None, wq_t=None):
+    import torch
+    N, K = w.shape
+    _need(w, "w", torch.bfloat16, (N, K))
+    wq = _out(wq, "wq", torch.uint8, (N, K), w)
+    ws = _out(ws, "ws", torch.float32, (N // 128, K // 128), w)
+    if transposed:
+        wq_t = _out(wq_t, "wq_t", torch.uint8, (K, N), w)
+    else:
+        wq_t = None
+    _check("quantize_weight_128x128", load_library().quantize_weight_128x128(
+        _ptr(w), N, K, _ptr(wq), _ptr(ws), _ptr(wq_t), _stream(w)))
+    return wq, ws, wq_t
+
+
+def transpose_quantize_128x1(x, xq_t=None, xs_t=None):
+    import torch
+    M, C = x.shape
+    _need(x, "x", torch.bfloat16, (M, C))
+    xq_t = _out(xq_t, "xq_t", torch.uint8, (C, M), x)
+    xs_t = _out(xs_t, "xs_t", torch.float32, (C, M // 128), x)
+    _check("transpose_quantize_128x1", load_library().transpose_quantize_128x1(
+        _ptr(x), M, C, _ptr(xq_t), _ptr(xs_t), _stream(x)))
+    return xq_t, xs_t
+
+
+def fp8_gemm_fwd(xq, xs, wq, ws, out=None):
+    import torch
+    M, K = xq.shape
+    N = wq.shape[0]
+    _need(xq, "xq", torch.uint8, (M, K))
+    _need(xs, "xs", torch.float32, (M, K // 128))
+    _need(wq, "wq", torch.uint8, (N, K))
+    _need(ws, "ws", torch.float32, (N // 128, K // 128))
+    y = _out(out, "out", torch.bfloat16, (M, N), xq)
+    _check("fp8_gemm_fwd", load_library().fp8_gemm_fwd(
+        _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y), M, N, K, _stream(xq)))
+    return y
+
+
+def fp8_gemm_dgrad(dyq, dys, wq_t, ws, out=None):
+    import torch
+    M, N = dyq.shape
+    K = wq_t.shape[0]
+    _need(dyq, "dyq", torch.uint8, (M, N))
+    _need(dys, "dys", torch.float32, (M, N // 128))
+    _need(wq_t, "wq_t", torch.uint8, (K, N))
+    _need(ws, "ws", torch.float32, (N // 128, K // 128))
+    dx = _out(out, "out", torch.bfloat16, (M, K), dyq)
+    _check("fp8_gemm_dgrad", load_library().fp8_gemm_dgrad(
+        _ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws), _ptr(dx), M, N, K, _stream(dyq)))
+    return dx
+
+
+def fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, out=None):
+    import torch
+    N, M = dyq_t.shape
+    K = xq_t.shape[0]
+    _need(dyq_t, "dyq_t", torch.uint8, (N, M))
+    _need(dys_t, "dys_t", torch.float32, (N, M // 128))
+    _need(xq_t, "xq_t", torch.uint8, (K, M))
+    _need(xs_t, "xs_t", torch.float32, (K, M // 128))
+    dw = _out(out, "out", torch.bfloat16, (N, K), dyq_t)
+    _check("fp8_gemm_wgrad", load_library().fp8_gemm_wgrad(
+        _ptr(dyq_t), _ptr(dys_t), _ptr(xq_t), _ptr(xs_t), _ptr(dw), M, N, K, _stream(dyq_t)))
+    return dw
+
+
+def cast_f32_e4m3(v, out=None):
+    import torch
+    (n,) = v.shape
+    _need(v, "v", torch.float32, (n,))
+    o = _out(out, "out", torch.uint8, (n,), v)
+    _check("fp8bsq_cast_f32_e4m3", load_library().fp8bsq_cast_f32_e4m3(
+        _ptr(v), _ptr(o), n, _stream(v)))
+    return o

@@ -1,0 +1,115 @@
+// The C ABI of the library: argument validation, then one launch per call.
+//
+// Every check runs before any HIP runtime call, so an invalid call returns its
+// status without touching the device or the stream.
+#include "../../include/fp8bsq.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // every dimension < 2^31
+constexpr int64_t kMaxElems = (int64_t)1 << 40;  // every tensor < 2^40 elements
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool dims_ok(int64_t a, int64_t b) {
+  if (a < 0 || b < 0 || a >= kMaxDim || b >= kMaxDim) return false;
+  return a == 0 || b < kMaxElems / a;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP8BSQ_OK : FP8BSQ_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8bsq_strerror(int status) {
+  switch (status) {
+    case FP8BSQ_OK: return "ok";
+    case FP8BSQ_ERR_NULL: return "a required pointer is NULL";
+    case FP8BSQ_ERR_SHAPE: return "unsupported shape (negative, too large, or not a multiple of 128 where required)";
+    case FP8BSQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case FP8BSQ_ERR_HIP: return "the HIP runtime reported an error at launch";
+    default: return "unknown status";
+  }
+}
+
+int fp8bsq_abi_version(void) { return FP8BSQ_ABI_VERSION; }
+
+int quantize_act_1x128(const void* x, int64_t M, int64_t K, uint8_t* xq, float* xs, void* stream) {
+  if (!dims_ok(M, K) || K % 128) return FP8BSQ_ERR_SHAPE;
+  if (M == 0 || K == 0) return FP8BSQ_OK;
+  if (!x || !xq || !xs) return FP8BSQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(xs)) return FP8BSQ_ERR_ALIGN;
+  return hip_status(fp8bsq::launch_quant_act_1x128(x, M, K, xq, xs, as_stream(stream)));
+}
+
+int quantize_weight_128x128(const void* w, int64_t N, int64_t K, uint8_t* wq, float* ws,
+                            uint8_t* wq_t, void* stream) {
+  if (!dims_ok(N, K) || N % 128 || K % 128) return FP8BSQ_ERR_SHAPE;
+  if (N == 0 || K == 0) return FP8BSQ_OK;
+  if (!w || !wq || !ws) return FP8BSQ_ERR_NULL;
+  if (!aligned16(w) || !aligned16(wq) || !aligned16(ws) || (wq_t && !aligned16(wq_t)))
+    return FP8BSQ_ERR_ALIGN;
+  return hip_status(fp8bsq::launch_quant_weight_128x128(w, N, K, wq, ws, wq_t, as_stream(stream)));
+}
+
+int transpose_quantize_128x1(const void* x, int64_t M, int64_t C, uint8_t* xq_t, float* xs_t,
+                             void* stream) {
+  if (!dims_ok(M, C) || M % 128 || C % 128) return FP8BSQ_ERR_SHAPE;
+  if (M == 0 || C == 0) return FP8BSQ_OK;
+  if (!x || !xq_t || !xs_t) return FP8BSQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xq_t) || !aligned16(xs_t)) return FP8BSQ_ERR_ALIGN;
+  return hip_status(fp8bsq::launch_transpose_quant_128x1(x, M, C, xq_t, xs_t, as_stream(stream)));
+}
+
+int fp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
+                 int64_t M, int64_t N, int64_t K, void* stream) {
+  if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N) || N % 128 || K % 128)
+    return FP8BSQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BSQ_OK;
+  if (K == 0) return FP8BSQ_ERR_SHAPE;  // an empty contraction would leave y unwritten
+  if (!xq || !xs || !wq || !ws || !y) return FP8BSQ_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws) || !aligned16(y))
+    return FP8BSQ_ERR_ALIGN;
+  return hip_status(fp8bsq::launch_gemm_fwd(xq, xs, wq, ws, y, M, N, K, as_stream(stream)));
+}
+
+int fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
+                   void* dx, int64_t M, int64_t N, int64_t K, void* stream) {
+  if (!dims_ok(M, N) || !dims_ok(K, N) || !dims_ok(M, K) || N % 128 || K % 128)
+    return FP8BSQ_ERR_SHAPE;
+  if (M == 0 || K == 0) return FP8BSQ_OK;
+  if (N == 0) return FP8BSQ_ERR_SHAPE;
+  if (!dyq || !dys || !wq_t || !ws || !dx) return FP8BSQ_ERR_NULL;
+  if (!aligned16(dyq) || !aligned16(dys) || !aligned16(wq_t) || !aligned16(ws) || !aligned16(dx))
+    return FP8BSQ_ERR_ALIGN;
+  return hip_status(fp8bsq::launch_gemm_dgrad(dyq, dys, wq_t, ws, dx, M, N, K, as_stream(stream)));
+}
+
+int fp8_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t, const float* xs_t,
+                   void* dw, int64_t M, int64_t N, int64_t K, void* stream) {
+  if (!dims_ok(N, M) || !dims_ok(K, M) || !dims_ok(N, K) || M % 128 || N % 128 || K % 128)
+    return FP8BSQ_ERR_SHAPE;
+  if (N == 0 || K == 0) return FP8BSQ_OK;
+  if (M == 0) return FP8BSQ_ERR_SHAPE;
+  if (!dyq_t || !dys_t || !xq_t || !xs_t || !dw) return FP8BSQ_ERR_NULL;
+  if (!aligned16(dyq_t) || !aligned16(dys_t) || !aligned16(xq_t) || !aligned16(xs_t) || !aligned16(dw))
+    return FP8BSQ_ERR_ALIGN;
+  return hip_status(fp8bsq::launch_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, dw, M, N, K, as_stream(stream)));
+}
+
+int fp8bsq_cast_f32_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {
+  if (n < 0 || n >= kMaxElems || n % 4) return FP8BSQ_ERR_SHAPE;
+  if (n == 0) return FP8BSQ_OK;
+  if (!in || !out) return FP8BSQ_ERR_NULL;
+  if (!aligned16(in) || !aligned16(out)) return FP8BSQ_ERR_ALIGN;
+  return hip_status(fp8bsq::launch_cast_f32_e4m3(in, out, n, as_stream(stream)));
+}
+
+}  // extern "C"

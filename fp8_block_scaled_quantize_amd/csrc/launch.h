@@ -1,0 +1,29 @@
+// Kernel launchers of the library (internal). Each enqueues on `stream` and
+// returns hipGetLastError(); shapes and pointers are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bsq {
+
+hipError_t launch_quant_act_1x128(const void* x, int64_t M, int64_t K, uint8_t* xq, float* xs,
+                                  hipStream_t stream);
+hipError_t launch_quant_weight_128x128(const void* w, int64_t N, int64_t K, uint8_t* wq, float* ws,
+                                       uint8_t* wq_t, hipStream_t stream);
+hipError_t launch_transpose_quant_128x1(const void* x, int64_t M, int64_t C, uint8_t* xq_t,
+                                        float* xs_t, hipStream_t stream);
+hipError_t launch_cast_f32_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+
+// GEMM roles. All three run the same NT kernel family: D[i][j] = sum_k P[i,k] Q[j,k]
+// written to out[j][i]; they differ in operands and in how the P scale is indexed.
+hipError_t launch_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                           void* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t,
+                             const float* ws, void* dx, int64_t M, int64_t N, int64_t K,
+                             hipStream_t stream);
+hipError_t launch_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t,
+                             const float* xs_t, void* dw, int64_t M, int64_t N, int64_t K,
+                             hipStream_t stream);
+
+}  // namespace fp8bsq

@@ -1,0 +1,310 @@
+// Quantizer kernels: 1x128 row groups, 128x128 blocks, 128x1 transposed groups.
+//
+// Source: Resumen Técnico: Jet-RL (gist.science), "Esquema de Cuantización":
+// activations in 1x128 groups, weights in 128x128 blocks, WGrad operands in
+// 1x128 / 128x1 groups along the tokens, saved activations in FP8.
+//
+// All three are HBM-bound streaming kernels: every bf16 element is read once
+// with 16-byte coalesced loads and every E4M3 byte written once. The group
+// amax is reduced inside the wavefront with DPP moves; the 128x1 kernel
+// transposes its output tile through LDS so both its reads and its writes
+// stay coalesced.
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8bsq {
+
+// ============================================================================
+// 1x128: a [M, K] tensor with K % 128 == 0 is a flat array of G = M*K/128
+// groups of 128 contiguous elements, and group g's scale is xs[g]. Each group
+// is handled by 8 lanes; lane j holds elements 8j..8j+7 and 64+8j..64+8j+7,
+// so each load instruction reads 128 contiguous bytes per group.
+// ============================================================================
+constexpr int ACT_THREADS = 256;
+constexpr int ACT_PASSES = 2;
+constexpr int ACT_GROUPS_PER_PASS = ACT_THREADS / 8;
+constexpr int ACT_GROUPS_PER_BLOCK = ACT_GROUPS_PER_PASS * ACT_PASSES;
+
+__device__ __forceinline__ void unpack8(const u32x4& r, float* v) {
+  v[0] = bf16_lo(r[0]); v[1] = bf16_hi(r[0]);
+  v[2] = bf16_lo(r[1]); v[3] = bf16_hi(r[1]);
+  v[4] = bf16_lo(r[2]); v[5] = bf16_hi(r[2]);
+  v[6] = bf16_lo(r[3]); v[7] = bf16_hi(r[3]);
+}
+
+__global__ __launch_bounds__(ACT_THREADS) void quant_act_1x128_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, float* __restrict__ xs, int64_t G) {
+  const int t = threadIdx.x;
+  const int j = t & 7;
+  u32x4 raw[ACT_PASSES][2];
+  int64_t grp[ACT_PASSES];
+#pragma unroll
+  for (int p = 0; p < ACT_PASSES; ++p) {
+    const int64_t g = (int64_t)blockIdx.x * ACT_GROUPS_PER_BLOCK + p * ACT_GROUPS_PER_PASS + (t >> 3);
+    grp[p] = g;
+    const int64_t gc = g < G ? g : G - 1;  // tail lanes re-read the last group; they store nothing
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + gc * 128);
+    raw[p][0] = __builtin_nontemporal_load(src + j);
+    raw[p][1] = __builtin_nontemporal_load(src + j + 8);
+  }
+#pragma unroll
+  for (int p = 0; p < ACT_PASSES; ++p) {
+    float v[16];
+    unpack8(raw[p][0], v);
+    unpack8(raw[p][1], v + 8);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = max8(m);
+    const float s = group_scale(m);
+    const GroupDiv d = group_div(m, s);
+    if (m < 0x1p-64f) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] *= d.xmul;
+    }
+    float q[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = quotient(v[i], d.sc, d.r);
+    const u32x2 lo = u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
+    const u32x2 hi = u32x2{e4m3x4(q[8], q[9], q[10], q[11]), e4m3x4(q[12], q[13], q[14], q[15])};
+    const int64_t g = grp[p];
+    if (g < G) {
+      u32x2* dst = reinterpret_cast<u32x2*>(xq + g * 128);
+      __builtin_nontemporal_store(lo, dst + j);
+      __builtin_nontemporal_store(hi, dst + j + 8);
+      if (j == 0) xs[g] = s;
+    }
+  }
+}
+
+// ============================================================================
+// 128x128: one workgroup per block. Thread t holds an 8x8 sub-tile: rows
+// 8*(t/16) .. +7 and columns 8*(t%16) .. +7 of the block (eight 16-byte row
+// loads). The block amax is reduced across the wavefront with DPP and
+// shuffles, then across the four wavefronts through LDS. The optional
+// transposed copy is produced by an 8x8 byte transpose in registers.
+// ============================================================================
+constexpr int W_THREADS = 256;
+
+// 4x4 byte transpose: r[i] byte j -> c[j] byte i.
+__device__ __forceinline__ void transpose4x4(const uint32_t r[4], uint32_t c[4]) {
+  const uint32_t p01l = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);
+  const uint32_t p01h = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);
+  const uint32_t p23l = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
+  const uint32_t p23h = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
+  c[0] = __builtin_amdgcn_perm(p23l, p01l, 0x05040100u);
+  c[1] = __builtin_amdgcn_perm(p23l, p01l, 0x07060302u);
+  c[2] = __builtin_amdgcn_perm(p23h, p01h, 0x05040100u);
+  c[3] = __builtin_amdgcn_perm(p23h, p01h, 0x07060302u);
+}
+
+__global__ __launch_bounds__(W_THREADS) void quant_weight_128x128_kernel(
+    const uint16_t* __restrict__ w, uint8_t* __restrict__ wq, float* __restrict__ ws,
+    uint8_t* __restrict__ wq_t, int N, int K) {
+  __shared__ float red[W_THREADS / 64];
+  const int t = threadIdx.x;
+  const int kb = blockIdx.x, nb = blockIdx.y;
+  const int r0 = 8 * (t >> 4), c0 = 8 * (t & 15);
+  const int64_t row0 = (int64_t)nb * 128 + r0;
+  const int64_t col0 = (int64_t)kb * 128 + c0;
+
+  u32x4 raw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w + (row0 + i) * K + col0));
+
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v[8];
+    unpack8(raw[i], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+  }
+  m = max64(m);
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = group_scale(m);
+  const GroupDiv d = group_div(m, s);
+  const bool tiny = m < 0x1p-64f;
+
+  uint32_t code[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v[8];
+    unpack8(raw[i], v);
+    if (tiny) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= d.xmul;
+    }
+    float q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = quotient(v[e], d.sc, d.r);
+    code[i][0] = e4m3x4(q[0], q[1], q[2], q[3]);
+    code[i][1] = e4m3x4(q[4], q[5], q[6], q[7]);
+    __builtin_nontemporal_store(u32x2{code[i][0], code[i][1]},
+                                reinterpret_cast<u32x2*>(wq + (row0 + i) * K + col0));
+  }
+  if (t == 0) ws[(int64_t)nb * (K / 128) + kb] = s;
+
+  if (wq_t != nullptr) {
+    // Transpose the 8x8 byte tile: out[j] holds column c0+j, rows r0..r0+7.
+    uint32_t out[8][2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {      // column bytes 0-3 / 4-7
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh) {          // rows 0-3 / 4-7
+        uint32_t r[4], c[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = code[4 * rh + i][half];
+        transpose4x4(r, c);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) out[4 * half + jj][rh] = c[jj];
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      __builtin_nontemporal_store(u32x2{out[jj][0], out[jj][1]},
+                                  reinterpret_cast<u32x2*>(wq_t + (col0 + jj) * N + row0));
+  }
+}
+
+// ============================================================================
+// 128x1 transposed: tile = 128 tokens x 64 channels per workgroup. Thread t
+// reads channels 8*(t%8) .. +7 of tokens 4*(t/8) .. +3 (16-byte loads, 128
+// contiguous bytes per token row). Channel amax: in-thread over 4 tokens,
+// across the 8 lanes of a wavefront that share the channels, then across the
+// 4 wavefronts through LDS. One wavefront computes the 64 channel scales; the
+// codes go to an LDS tile [64 channels][128 tokens] and leave as 128-byte rows
+// of xq_t.
+// ============================================================================
+constexpr int T_THREADS = 256;
+constexpr int T_CH = 64;
+constexpr int T_ROW_BYTES = 128 + 4;  // padded LDS row of the transposed code tile
+
+__global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ xq_t, float* __restrict__ xs_t,
+    int M, int C) {
+  __shared__ float red[4][T_CH];
+  __shared__ float p_sc[T_CH], p_r[T_CH], p_mul[T_CH];
+  __shared__ __align__(16) uint8_t tile[T_CH * T_ROW_BYTES];
+
+  const int t = threadIdx.x;
+  const int cb = blockIdx.x, mb = blockIdx.y;
+  const int cc = t & 7;           // channel chunk: channels 8cc .. 8cc+7 of the tile
+  const int tr = 4 * (t >> 3);    // first token of this thread's four
+  const int64_t c0 = (int64_t)cb * T_CH;
+  const int64_t m0 = (int64_t)mb * 128;
+
+  u32x4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    raw[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(x + (m0 + tr + i) * C + c0 + 8 * cc));
+
+  float v[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) unpack8(raw[i], v[i]);
+  float cm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float mm = fmaxf(fmaxf(fabsf(v[0][e]), fabsf(v[1][e])), fmaxf(fabsf(v[2][e]), fabsf(v[3][e])));
+    // lanes with equal (lane % 8) share channels: reduce over lane bits 3..5
+    mm = fmaxf(mm, dpp_f<0x128>(mm));               // row_ror:8  (lane ^ 8 within a row of 16)
+    mm = fmaxf(mm, __shfl_xor(mm, 16, 64));
+    mm = fmaxf(mm, __shfl_xor(mm, 32, 64));
+    cm[e] = mm;
+  }
+  const int wave = t >> 6, lane = t & 63;
+  if (lane < 8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave][8 * lane + e] = cm[e];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int c = lane;
+    const float m = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+    const float s = group_scale(m);
+    const GroupDiv d = group_div(m, s);
+    p_sc[c] = d.sc;
+    p_r[c] = d.r;
+    p_mul[c] = d.xmul;
+    xs_t[(c0 + c) * (M / 128) + mb] = s;
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = 8 * cc + e;
+    const float sc = p_sc[c], r = p_r[c], mul = p_mul[c];
+    float q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = quotient(v[i][e] * mul, sc, r);
+    *reinterpret_cast<uint32_t*>(tile + c * T_ROW_BYTES + tr) = e4m3x4(q[0], q[1], q[2], q[3]);
+  }
+  __syncthreads();
+
+  // 64 rows x 128 bytes = 512 16-byte pieces, two per thread, 8 lanes per row.
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = (t >> 3) + 32 * h;
+    const int seg = t & 7;
+    const uint8_t* src = tile + row * T_ROW_BYTES + 16 * seg;
+    const u32x4 val = u32x4{*reinterpret_cast<const uint32_t*>(src),
+                            *reinterpret_cast<const uint32_t*>(src + 4),
+                            *reinterpret_cast<const uint32_t*>(src + 8),
+                            *reinterpret_cast<const uint32_t*>(src + 12)};
+    __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(xq_t + (c0 + row) * M + m0 + 16 * seg));
+  }
+}
+
+// ============================================================================
+// Plain encoder: 4 fp32 values -> 4 E4M3 bytes per thread.
+// ============================================================================
+__global__ __launch_bounds__(256) void cast_f32_e4m3_kernel(const f32x4* __restrict__ in,
+                                                          uint32_t* __restrict__ out, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) {
+    const f32x4 v = in[i];
+    out[i] = e4m3x4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// ============================================================================
+// Launchers (shapes validated by the caller).
+// ============================================================================
+hipError_t launch_quant_act_1x128(const void* x, int64_t M, int64_t K, uint8_t* xq, float* xs,
+                                  hipStream_t stream) {
+  const int64_t G = M * (K / 128);
+  const int64_t blocks = (G + ACT_GROUPS_PER_BLOCK - 1) / ACT_GROUPS_PER_BLOCK;
+  hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)blocks), dim3(ACT_THREADS), 0, stream,
+                     static_cast<const uint16_t*>(x), xq, xs, G);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_128x128(const void* w, int64_t N, int64_t K, uint8_t* wq, float* ws,
+                                       uint8_t* wq_t, hipStream_t stream) {
+  hipLaunchKernelGGL(quant_weight_128x128_kernel, dim3((unsigned)(K / 128), (unsigned)(N / 128)),
+                     dim3(W_THREADS), 0, stream, static_cast<const uint16_t*>(w), wq, ws, wq_t,
+                     (int)N, (int)K);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_quant_128x1(const void* x, int64_t M, int64_t C, uint8_t* xq_t,
+                                        float* xs_t, hipStream_t stream) {
+  hipLaunchKernelGGL(transpose_quant_128x1_kernel, dim3((unsigned)(C / T_CH), (unsigned)(M / 128)),
+                     dim3(T_THREADS), 0, stream, static_cast<const uint16_t*>(x), xq_t, xs_t,
+                     (int)M, (int)C);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_f32_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
+  const int64_t n4 = n / 4;
+  const int64_t blocks = (n4 + 255) / 256;
+  hipLaunchKernelGGL(cast_f32_e4m3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const f32x4*>(in), reinterpret_cast<uint32_t*>(out), n4);
+  return hipGetLastError();
+}
+
+}  // namespace fp8bsq

@@ -137,11 +137,17 @@ def _small_grid():
 SMALL_GRID = _small_grid()
 
 
-def exact_operand(rng, rows, cols, block_exp):
+# Values 448 * 2^-j (j = 0..2) and 0: products are multiples of 448^2 / 16, so
+# every partial sum of up to 2048 terms needs at most 16 significant bits.
+NARROW_GRID = np.array([0.0, 112.0, 224.0, 448.0], dtype=np.float32)
+
+
+def exact_operand(rng, rows, cols, block_exp, grid=None):
     """bf16 bits of a [rows, cols] tensor built so that FP8 quantization is lossless.
 
     ``block_exp`` is an int array [rows/128, cols/128]; every element of block
-    (i, j) is v * 2^block_exp[i, j] with v drawn from SMALL_GRID (random sign),
+    (i, j) is v * 2^block_exp[i, j] with v drawn from ``grid`` (SMALL_GRID by
+    default; random sign),
     and the elements with r % 128 == c % 128 are +-448 * 2^block_exp[i, j].
     Every 1x128 row group, 128x1 column group and 128x128 block therefore has
     amax exactly 448 * 2^e, so its scale is the power of two 2^e and every
@@ -149,10 +155,46 @@ def exact_operand(rng, rows, cols, block_exp):
     """
     if rows % GROUP or cols % GROUP:
         raise ValueError("rows and cols must be multiples of 128")
-    v = rng.choice(SMALL_GRID, size=(rows, cols)).astype(np.float32)
+    v = rng.choice(SMALL_GRID if grid is None else grid, size=(rows, cols)).astype(np.float32)
     diag = (np.arange(rows)[:, None] % GROUP) == (np.arange(cols)[None, :] % GROUP)
     v = np.where(diag, np.float32(448.0), v)
     v *= rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=(rows, cols))
     e = np.repeat(np.repeat(np.asarray(block_exp, dtype=np.int64), GROUP, axis=0), GROUP, axis=1)
     v = v * np.exp2(e).astype(np.float32)
     return f32_to_bf16_bits(v)
+
+
+# ---------------------------------------------------------------------------
+# Device-side generator for full-size tensors (same recipe, torch's Philox
+# generator on the GPU). Used where a tensor is too large to draw on the host
+# quickly; tests copy the slices they check back to the host.
+# ---------------------------------------------------------------------------
+
+def bf16_normal_device(shape, std, outlier_frac=0.0, seed=0, device="cuda", outlier_gain=20.0):
+    """bf16 torch tensor of N(0, std^2) values with optional outlier columns, drawn on `device`."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    x.mul_(std)
+    if outlier_frac > 0:
+        C = shape[-1]
+        n_out = int(round(outlier_frac * C))
+        gc = torch.Generator(device="cpu")
+        gc.manual_seed(int(seed) + 1)
+        cols = torch.randperm(C, generator=gc)[:n_out].to(device)
+        x[..., cols] *= outlier_gain
+    return x.to(torch.bfloat16)
+
+
+def linear_tensors_device(lin, seed=0, which=("x", "w", "dy"), device="cuda"):
+    """Device bf16 tensors x [M,K], w [N,K], dy [M,N] of one linear (seeds seed, seed+10, seed+20)."""
+    M, N, K = lin["M"], lin["N"], lin["K"]
+    out = {}
+    if "x" in which:
+        out["x"] = bf16_normal_device((M, K), lin["x_std"], 0.01 if lin["x_outliers"] else 0.0, seed, device)
+    if "w" in which:
+        out["w"] = bf16_normal_device((N, K), lin["w_std"], 0.0, seed + 10, device)
+    if "dy" in which:
+        out["dy"] = bf16_normal_device((M, N), lin["dy_std"], 0.01 if lin["dy_outliers"] else 0.0, seed + 20, device)
+    return out

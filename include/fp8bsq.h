@@ -1,0 +1,166 @@
+/*
+ * fp8bsq.h -- C ABI of the MI355X (gfx950) FP8 block-scaled linear-layer library.
+ *
+ * What it computes (Resumen Técnico: Jet-RL, gist.science, section "Esquema de
+ * Cuantización"; and "Arquitectura Central" for the shared forward/rollout flow):
+ * the linear layers run as FP8 GEMMs; activations are quantized in 1x128
+ * per-token groups and weights in 128x128 blocks; DGrad and WGrad also run in
+ * FP8, WGrad on operands grouped 1x128 / 128x1 along the token dimension;
+ * gradients entering and leaving the GEMMs are bf16; master weights are bf16.
+ *
+ * Numeric format (fixed by this library; the pages only say "FP8"):
+ *   - FP8 codes are OCP E4M3 ("E4M3FN": bias 7, max finite 448, NaN 0x7F/0xFF,
+ *     signed zero, subnormals k*2^-9), one byte per element;
+ *   - one fp32 scale per group: s = fl32(amax / 448), or 1.0 for an all-zero
+ *     group; each element is stored as E4M3_RNE(fl32(x / s)) -- one IEEE fp32
+ *     division, then round-to-nearest-even to E4M3, with gradual underflow;
+ *   - GEMMs multiply E4M3 codes exactly, accumulate in fp32, apply the two
+ *     operand scales once per 128-long block of the contraction dimension,
+ *     and round the result to bf16 (nearest even).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers (HIP device memory) owned by the
+ *     caller. Tensors are dense and row-major. bf16 tensors are passed as
+ *     void* (16-bit elements). The library allocates nothing and keeps no
+ *     pointer after returning.
+ *   - Every pointer must be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     Calls only enqueue work on that stream and return; outputs are valid
+ *     once the stream has reached that point. The library never synchronizes.
+ *   - Outputs must not overlap inputs. Outputs are fully overwritten.
+ *   - Results are deterministic: the same inputs, shape and library build give
+ *     identical bytes.
+ *   - Return value: FP8BSQ_OK (0), or an error code below. Arguments are
+ *     validated before any HIP runtime call, so an invalid call touches
+ *     neither the device nor the stream. No C++ exception crosses the ABI.
+ *   - Sizes are int64_t; every dimension must be >= 0 and < 2^31, and every
+ *     tensor must hold fewer than 2^40 elements. A call with a zero-sized
+ *     output is a valid no-op.
+ *   - Thread-safe and reentrant (no mutable global state).
+ */
+#ifndef FP8BSQ_H
+#define FP8BSQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8BSQ_ABI_VERSION 1
+
+/* Status codes. */
+#define FP8BSQ_OK 0
+#define FP8BSQ_ERR_NULL 1      /* a required pointer is NULL                          */
+#define FP8BSQ_ERR_SHAPE 2     /* a dimension is negative, too large or not a multiple of 128 where required */
+#define FP8BSQ_ERR_ALIGN 3     /* a pointer is not 16-byte aligned                    */
+#define FP8BSQ_ERR_HIP 4       /* the HIP runtime reported an error at launch         */
+
+/* Returns a static, human-readable description of a status code. */
+const char* fp8bsq_strerror(int status);
+
+/* Returns FP8BSQ_ABI_VERSION of the built library. */
+int fp8bsq_abi_version(void);
+
+/*
+ * quantize_act_1x128 -- 1x128 per-token group quantization.
+ * Source: "Esquema de Cuantización", activations bullet (1x128 groups); also
+ * applied to dY before DGrad (backward GEMMs run in FP8, gradients arrive bf16).
+ *
+ *   x   in : bf16 [M, K]
+ *   xq  out: E4M3 [M, K]           xq[m, k] = E4M3_RNE(fl32(x[m, k] / xs[m, k/128]))
+ *   xs  out: fp32 [M, K/128]       xs[m, g] = scale of x[m, 128g : 128g+128]
+ * Shape: K % 128 == 0; M >= 0 (any).
+ */
+int quantize_act_1x128(const void* x, int64_t M, int64_t K,
+                       uint8_t* xq, float* xs, void* stream);
+
+/*
+ * quantize_weight_128x128 -- 128x128 per-block weight quantization.
+ * Source: "Esquema de Cuantización", weights bullet (128x128 blocks);
+ * "Arquitectura Central": the bf16 master weights are what gets quantized.
+ *
+ *   w    in : bf16 [N, K]
+ *   wq   out: E4M3 [N, K]
+ *   ws   out: fp32 [N/128, K/128]  ws[i, j] = scale of block w[128i:128i+128, 128j:128j+128]
+ *   wq_t out: E4M3 [K, N] or NULL  the byte transpose of wq (the DGrad operand;
+ *                                   a block's amax is transpose-invariant)
+ * Shape: N % 128 == 0, K % 128 == 0.
+ */
+int quantize_weight_128x128(const void* w, int64_t N, int64_t K,
+                            uint8_t* wq, float* ws, uint8_t* wq_t, void* stream);
+
+/*
+ * transpose_quantize_128x1 -- 128x1 token-group quantization, written transposed.
+ * Source: "Esquema de Cuantización", backward bullets: WGrad runs in FP8 with
+ * 1x128 / 128x1 operand groups; activations saved for backward are FP8.
+ *
+ *   x    in : bf16 [M, C]
+ *   xq_t out: E4M3 [C, M]          xq_t[c, m] = code of x[m, c]
+ *   xs_t out: fp32 [C, M/128]      xs_t[c, b] = scale of x[128b : 128b+128, c]
+ * Bit-identical to quantize_act_1x128 applied to the transpose of x.
+ * Shape: M % 128 == 0, C % 128 == 0.
+ */
+int transpose_quantize_128x1(const void* x, int64_t M, int64_t C,
+                             uint8_t* xq_t, float* xs_t, void* stream);
+
+/*
+ * fp8_gemm_fwd -- forward / rollout GEMM, Y = Xq . Wq^T.
+ * Source: "Esquema de Cuantización" (linear layers as FP8 GEMMs on 1x128
+ * activations and 128x128 weights); "Arquitectura Central" (rollout and
+ * training forward share this one flow).
+ *
+ *   xq in : E4M3 [M, K], xs in: fp32 [M, K/128]       (from quantize_act_1x128)
+ *   wq in : E4M3 [N, K], ws in: fp32 [N/128, K/128]   (from quantize_weight_128x128)
+ *   y  out: bf16 [M, N]
+ *   y[m, n] = bf16( sum_kb xs[m,kb] * ws[n/128,kb] * sum_{k in kb} xq[m,k]*wq[n,k] )
+ * Shape: N % 128 == 0, K % 128 == 0, M >= 0 (any).
+ */
+int fp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                 void* y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * fp8_gemm_dgrad -- DGrad, dX = dYq . Wq (contraction over N).
+ * Source: "Esquema de Cuantización", backward bullets (DGrad in FP8; bf16
+ * gradients between operators).
+ *
+ *   dyq  in : E4M3 [M, N], dys in: fp32 [M, N/128]    (quantize_act_1x128 of dY)
+ *   wq_t in : E4M3 [K, N]                              (wq_t of quantize_weight_128x128)
+ *   ws   in : fp32 [N/128, K/128]                      (the same forward block scales)
+ *   dx   out: bf16 [M, K]
+ *   dx[m, k] = bf16( sum_nb dys[m,nb] * ws[nb,k/128] * sum_{n in nb} dyq[m,n]*wq_t[k,n] )
+ * Shape: N % 128 == 0, K % 128 == 0, M >= 0 (any).
+ */
+int fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
+                   void* dx, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * fp8_gemm_wgrad -- WGrad, dW = dYq^T . Xq (contraction over the M tokens).
+ * Source: "Esquema de Cuantización", backward bullets (WGrad in FP8 with
+ * 1x128 and 128x1 groupings: both operands grouped along the tokens).
+ *
+ *   dyq_t in : E4M3 [N, M], dys_t in: fp32 [N, M/128]  (transpose_quantize_128x1 of dY)
+ *   xq_t  in : E4M3 [K, M], xs_t  in: fp32 [K, M/128]  (transpose_quantize_128x1 of X)
+ *   dw    out: bf16 [N, K]
+ *   dw[n, k] = bf16( sum_mb dys_t[n,mb] * xs_t[k,mb] * sum_{m in mb} dyq_t[n,m]*xq_t[k,m] )
+ * Shape: M % 128 == 0, N % 128 == 0, K % 128 == 0.
+ */
+int fp8_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t, const float* xs_t,
+                   void* dw, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * fp8bsq_cast_f32_e4m3 -- the library's E4M3 encoder on its own.
+ * Rounds each fp32 value to E4M3, nearest, ties to even, sign kept; the same
+ * device routine every quantizer uses after its division. Inputs must be
+ * finite with |v| <= 464 (the largest magnitude with a finite nearest code);
+ * other inputs give unspecified bytes.
+ *
+ *   in  in : fp32 [n];  out out: E4M3 [n].  n >= 0 and n % 4 == 0.
+ */
+int fp8bsq_cast_f32_e4m3(const float* in, uint8_t* out, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BSQ_H */

@@ -1,0 +1,102 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and rejects invalid arguments with the documented status before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bsq.h")
+LIB = os.path.join(ROOT, "fp8_block_scaled_quantize_amd", "libfp8bsq.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from fp8_block_scaled_quantize_amd.build import build
+        build()
+    return ctypes.CDLL(LIB)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"quantize_act_1x128", "quantize_weight_128x128", "transpose_quantize_128x1",
+                          "fp8_gemm_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
+                          "fp8bsq_strerror", "fp8bsq_abi_version", "fp8bsq_cast_f32_e4m3"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror(lib):
+    lib.fp8bsq_abi_version.restype = ctypes.c_int
+    assert lib.fp8bsq_abi_version() == 1
+    lib.fp8bsq_strerror.restype = ctypes.c_char_p
+    lib.fp8bsq_strerror.argtypes = [ctypes.c_int]
+    for code in range(5):
+        assert lib.fp8bsq_strerror(code)
+    assert lib.fp8bsq_strerror(99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+I64 = ctypes.c_int64
+FAKE = P(0x10000)        # aligned, never dereferenced: validation fails first or no launch happens
+MISALIGNED = P(0x10008)
+
+
+def test_quantizer_validation(lib):
+    q = lib.quantize_act_1x128
+    q.argtypes = [P, I64, I64, P, P, P]
+    assert q(FAKE, 4, 100, FAKE, FAKE, None) == 2          # K not a multiple of 128
+    assert q(FAKE, -1, 128, FAKE, FAKE, None) == 2         # negative
+    assert q(FAKE, 1 << 31, 128, FAKE, FAKE, None) == 2    # too large
+    assert q(None, 4, 128, FAKE, FAKE, None) == 1          # null
+    assert q(FAKE, 4, 128, MISALIGNED, FAKE, None) == 3    # misaligned
+    assert q(None, 0, 128, None, None, None) == 0          # empty: no-op
+    w = lib.quantize_weight_128x128
+    w.argtypes = [P, I64, I64, P, P, P, P]
+    assert w(FAKE, 100, 128, FAKE, FAKE, None, None) == 2
+    assert w(FAKE, 128, 128, None, FAKE, None, None) == 1
+    assert w(FAKE, 128, 128, FAKE, FAKE, MISALIGNED, None) == 3
+    t = lib.transpose_quantize_128x1
+    t.argtypes = [P, I64, I64, P, P, P]
+    assert t(FAKE, 64, 128, FAKE, FAKE, None) == 2         # M must be a multiple of 128
+    assert t(FAKE, 128, 64, FAKE, FAKE, None) == 2         # C too
+    assert t(FAKE, 128, 128, FAKE, None, None) == 1
+    c = lib.fp8bsq_cast_f32_e4m3
+    c.argtypes = [P, P, I64, P]
+    assert c(FAKE, FAKE, 6, None) == 2
+    assert c(None, FAKE, 8, None) == 1
+
+
+def test_gemm_validation(lib):
+    for name in ("fp8_gemm_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad"):
+        f = getattr(lib, name)
+        f.argtypes = [P, P, P, P, P, I64, I64, I64, P]
+        f.restype = ctypes.c_int
+        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 100, 128, None) == 2, name
+        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, 96, None) == 2, name
+        assert f(FAKE, FAKE, None, FAKE, FAKE, 128, 128, 128, None) == 1, name
+        assert f(FAKE, FAKE, FAKE, FAKE, MISALIGNED, 128, 128, 128, None) == 3, name
+    f = lib.fp8_gemm_wgrad
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 128, 128, None) == 2   # token dim grouped by 128
+    f = lib.fp8_gemm_fwd
+    assert f(None, None, None, None, None, 0, 128, 128, None) == 0    # M == 0: no-op
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 128, 0, None) == 2      # empty contraction
+
+
+def test_binding_has_no_cpu_fallback():
+    """The product package never imports the oracle and has no CPU compute path."""
+    pkg = os.path.join(ROOT, "fp8_block_scaled_quantize_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle|import_module\(.oracle|oracle\.", text, re.M), fn
