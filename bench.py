@@ -1,0 +1,253 @@
+"""Benchmark of the FP8 block-scaled linear-layer flow on one MI355X.
+
+One step = the whole hot path for every linear of the workload:
+    quantize_weight_128x128(W)            (with the transposed copy for DGrad)
+    quantize_act_1x128(X)      -> fp8_gemm_fwd      Y  = Xq Wq^T
+    quantize_act_1x128(dY)     -> fp8_gemm_dgrad    dX = dYq Wq
+    transpose_quantize_128x1(X), transpose_quantize_128x1(dY)
+                               -> fp8_gemm_wgrad    dW = dYq^T Xq
+on synthetic inputs already resident in HBM. Default workload: the four
+linears of a Qwen2.5-32B-shaped layer (qkv 5120->7168, o 5120->5120,
+up 5120->27648, down 27648->5120) at 32768 tokens.
+
+Prints ONE JSON line. `value` is GEMM TFLOP/s over the whole step (every
+quantizer and GEMM launch inside the timed region); per-kernel times come from
+HIP events recorded on the stream the kernels run on. `roofline` describes the
+kernel that takes the most time; `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME]
+                    [--no-cpu-baseline] [--traffic-from profiles/<file>.json]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOP/s (fwd/DGrad/WGrad), % of FP8 MFMA peak"
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA, published
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "qwen25_32b_linears_m32768"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-from", default=None,
+                    help="JSON with measured HBM bytes per launch of the dominant kernel")
+    return ap.parse_args()
+
+
+def act_bytes(rows, cols):
+    return rows * cols * 3 + rows * (cols // 128) * 4
+
+
+def weight_bytes(n, k, transposed):
+    return n * k * (4 if transposed else 3) + (n // 128) * (k // 128) * 4
+
+
+class Linear:
+    """Device buffers and the launch list of one linear layer."""
+
+    def __init__(self, lin, passes, seed, fq, inputs, torch):
+        self.name, self.M, self.N, self.K = lin["name"], lin["M"], lin["N"], lin["K"]
+        M, N, K = self.M, self.N, self.K
+        dev = "cuda"
+        t = inputs.linear_tensors_device(lin, seed=seed)
+        self.x, self.w, self.dy = t["x"], t["w"], t["dy"]
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+        u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+        self.passes = passes
+        dgrad, wgrad = "dgrad" in passes, "wgrad" in passes
+        self.wq, self.ws = e((N, K), u8), e((N // 128, K // 128), f32)
+        self.wq_t = e((K, N), u8) if dgrad else None
+        self.xq, self.xs = e((M, K), u8), e((M, K // 128), f32)
+        self.y = e((M, N), bf)
+        if dgrad:
+            self.dyq, self.dys = e((M, N), u8), e((M, N // 128), f32)
+            self.dx = e((M, K), bf)
+        if wgrad:
+            self.xq_t, self.xs_t = e((K, M), u8), e((K, M // 128), f32)
+            self.dyq_t, self.dys_t = e((N, M), u8), e((N, M // 128), f32)
+            self.dw = e((N, K), bf)
+        self.fq = fq
+
+    def launches(self):
+        """(kind, key, flops, bytes, callable) for every launch of one step, in order."""
+        fq, M, N, K = self.fq, self.M, self.N, self.K
+        L = []
+        L.append(("quant_weight", f"{self.name}.w[{N},{K}]", 0, weight_bytes(N, K, self.wq_t is not None),
+                  lambda: fq.quantize_weight_128x128(self.w, self.wq_t is not None, self.wq, self.ws, self.wq_t)))
+        L.append(("quant_act", f"{self.name}.x[{M},{K}]", 0, act_bytes(M, K),
+                  lambda: fq.quantize_act_1x128(self.x, self.xq, self.xs)))
+        L.append(("gemm_fwd", f"{self.name}.fwd[{M}x{N}x{K}]", 2 * M * N * K, M * K + N * K + 2 * M * N,
+                  lambda: fq.fp8_gemm_fwd(self.xq, self.xs, self.wq, self.ws, out=self.y)))
+        if "dgrad" in self.passes:
+            L.append(("quant_act", f"{self.name}.dy[{M},{N}]", 0, act_bytes(M, N),
+                      lambda: fq.quantize_act_1x128(self.dy, self.dyq, self.dys)))
+            L.append(("gemm_dgrad", f"{self.name}.dgrad[{M}x{K}x{N}]", 2 * M * N * K, M * N + N * K + 2 * M * K,
+                      lambda: fq.fp8_gemm_dgrad(self.dyq, self.dys, self.wq_t, self.ws, out=self.dx)))
+        if "wgrad" in self.passes:
+            L.append(("quant_transpose", f"{self.name}.x_t[{M},{K}]", 0, act_bytes(M, K),
+                      lambda: fq.transpose_quantize_128x1(self.x, self.xq_t, self.xs_t)))
+            L.append(("quant_transpose", f"{self.name}.dy_t[{M},{N}]", 0, act_bytes(M, N),
+                      lambda: fq.transpose_quantize_128x1(self.dy, self.dyq_t, self.dys_t)))
+            L.append(("gemm_wgrad", f"{self.name}.wgrad[{N}x{K}x{M}]", 2 * M * N * K, M * N + M * K + 2 * N * K,
+                      lambda: fq.fp8_gemm_wgrad(self.dyq_t, self.dys_t, self.xq_t, self.xs_t, out=self.dw)))
+        return L
+
+
+def cpu_baseline(inputs, wl):
+    """Time the CPU oracle on a bounded sample: every pass of the o-proj linear at 1024 tokens."""
+    import numpy as np
+    from oracle import gemm, quant
+
+    lin = dict(next(l for l in wl["linears"] if l["name"] == "o") if any(l["name"] == "o" for l in wl["linears"])
+               else wl["linears"][0])
+    lin["M"] = 1024
+    t = inputs.linear_tensors(lin, seed=0)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    M, N, K = lin["M"], lin["N"], lin["K"]
+    t0 = time.perf_counter()
+    xq, xs = quant.quantize_act_1x128(t["x"])
+    wq, ws, _ = quant.quantize_weight_128x128(t["w"])
+    dyq, dys = quant.quantize_act_1x128(t["dy"])
+    xq_t, xs_t = quant.transpose_quantize_128x1(t["x"])
+    dyq_t, dys_t = quant.transpose_quantize_128x1(t["dy"])
+    gemm.gemm_fwd(xq, xs, wq, ws)
+    gemm.gemm_dgrad(dyq, dys, wq, ws)
+    gemm.gemm_wgrad(dyq_t, dys_t, xq_t, xs_t)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2 * M * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{lin['name']} linear ({K}->{N}) at {M} tokens: all five quantizations and "
+                      f"fwd/dgrad/wgrad in fp64, {dt:.1f} s wall",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is "
+              "described in DESIGN.md and not measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_block_scaled_quantize_amd as fq
+    from fp8_block_scaled_quantize_amd import inputs
+
+    if not os.path.exists(fq.library_path()):
+        from fp8_block_scaled_quantize_amd.build import build
+        build()
+    fq.load_library()
+    wl = inputs.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    print(f"[bench] workload {args.workload}: generating inputs", file=sys.stderr, flush=True)
+    layers = [Linear(lin, wl["passes"], 1000 + 17 * i, fq, inputs, torch) for i, lin in enumerate(wl["linears"])]
+    launches = [l for layer in layers for l in layer.launches()]
+    torch.cuda.synchronize()
+
+    for s in range(args.warmup):
+        for _, _, _, _, fn in launches:
+            fn()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, (_, _, _, _, fn) in enumerate(launches):
+            ev[s][i][0].record(stream)
+            fn()
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # Per-launch average durations (ms) from the HIP events.
+    per = []
+    for i, (kind, key, flops, nbytes, _) in enumerate(launches):
+        ms = sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
+        per.append({"kind": kind, "key": key, "ms": ms, "flops": flops, "bytes": nbytes})
+    gemm_flops = sum(p["flops"] for p in per)
+    gemm_ms = sum(p["ms"] for p in per if p["flops"])
+    quant_ms = sum(p["ms"] for p in per if not p["flops"])
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    kernels = {}
+    for p in per:
+        if p["flops"]:
+            tf = p["flops"] / (p["ms"] * 1e-3) / 1e12
+            kernels[p["key"]] = {"ms": round(p["ms"], 4), "tflops": round(tf, 1),
+                                 "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+        else:
+            gbs = p["bytes"] / (p["ms"] * 1e-3) / 1e9
+            kernels[p["key"]] = {"ms": round(p["ms"], 4), "gbs": round(gbs, 1),
+                                 "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+    dom = max(per, key=lambda p: p["ms"])
+    if dom["flops"]:
+        achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_FP8_TFLOPS, 4)}
+    else:
+        achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = dom["key"]
+    roof["avg_ms"] = round(dom["ms"], 4)
+    roof["traffic"] = None
+    if args.traffic_from and os.path.exists(args.traffic_from):
+        tr = json.load(open(args.traffic_from))
+        if tr.get("kernel") == dom["key"]:
+            roof["traffic"] = tr.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {"workload": args.workload,
+                   "tokens": wl["linears"][0]["M"],
+                   "linears": {l["name"]: [l["N"], l["K"]] for l in wl["linears"]},
+                   "passes": list(wl["passes"])},
+        "pct_of_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "gemm_only_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
+        "gemm_ms_per_step": round(gemm_ms, 3),
+        "quant_ms_per_step": round(quant_ms, 3),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(inputs, wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

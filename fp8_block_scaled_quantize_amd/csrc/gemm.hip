@@ -71,24 +71,34 @@ struct GemmCfg {
   static constexpr int NT = 64 * WAVES_I * WAVES_J;
   static constexpr int P_LOADS = BI * 8 / NT;                    // 16-byte loads per thread
   static constexpr int Q_LOADS = BJ * 8 / NT;
-  static constexpr int PS_COUNT = PS_ROW ? BI : BI / 128;        // P scales per K step
+  static constexpr int ROWSC = BJ + (PS_ROW ? BI : 0);          // per-row scales per K step
+  static constexpr int BLKSC = PS_ROW ? 0 : BI / 128;            // 128x128-block P scales per K step
   static constexpr int TILE_BYTES = (BI + BJ) * 128;
-  static constexpr int SCALE_FLOATS = BJ + PS_COUNT;
   static_assert(BI * 8 % NT == 0 && BJ * 8 % NT == 0, "loads must divide evenly");
-  static_assert(NT >= BJ + PS_COUNT, "one scale load per thread at most");
+  static_assert(NT >= ROWSC && BLKSC <= 64, "one scale load per thread at most");
   static_assert(PS_ROW || (128 % WI == 0), "a block-scaled wavefront must sit inside one 128-row block");
   static_assert(BI % 128 == 0, "BI must be a multiple of 128");
 };
 
 // Byte offset of 16-byte chunk `chunk` of tile row `row` (rows are 128 bytes).
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// The chunk index is XORed with f(row) = (row & 7) ^ ((row >> 3) & 1), so that
+// the MFMA fragment reads (one 16-byte chunk from each of 16 consecutive rows
+// per 16 lanes) hit distinct banks whether the LDS serves 8 lanes x 16 bytes
+// or 16 lanes x 16 bytes per clock: any 8 aligned consecutive rows get 8
+// distinct chunk slots, and the even and the odd rows of any 16 aligned
+// consecutive rows each get 8 distinct slots.
+__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_key(row)) << 4); }
 
 template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW>
 __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses LDS address-space casts, device pass only
   using C = GemmCfg<WAVES_I, WAVES_J, SI, SJ, PS_ROW>;
   __shared__ __align__(16) uint8_t tiles[2][C::TILE_BYTES];
-  __shared__ __align__(16) float scales[2][C::SCALE_FLOATS];
+  // Per-row scales come in groups of 4 K steps, [row][4], double-buffered by
+  // group; block P scales come per K step.
+  __shared__ __align__(16) float rowsc[2][C::ROWSC * 4];
+  __shared__ __align__(16) float blksc[2][C::BLKSC > 0 ? C::BLKSC : 1];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -97,59 +107,72 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
 
   int ti, tj;
   map_tile(blockIdx.x, gridDim.x, p.tiles_i, p.tiles_j, ti, tj);
-  const int i0 = ti * C::BI, j0 = tj * C::BJ;
+  // The last tile along a dimension is shifted back to end at the edge, so
+  // every row it loads exists; where it overlaps its neighbour both compute
+  // and store the same values. Only a dimension smaller than one tile needs
+  // clamped rows (their outputs are never stored).
+  const int i0 = p.I >= C::BI ? min(ti * C::BI, p.I - C::BI) : 0;
+  const int j0 = p.J >= C::BJ ? min(tj * C::BJ, p.J - C::BJ) : 0;
+  const int prows = min(p.I - i0, C::BI);
+  const int qrows = min(p.J - j0, C::BJ);
 
   // ---- global -> LDS loads. Each wavefront instruction moves 64 x 16 bytes
-  //      straight into 1 KB of LDS (8 tile rows), lane L landing at byte 16L.
-  //      Lane L therefore fetches the global chunk that the swizzled layout
-  //      keeps at that spot: row 8n + L/8, logical chunk (L%8) ^ (L/8).
-  //      Rows past the end are clamped into range; they feed only outputs
-  //      that are never stored. ----
-  constexpr int P_INSTR = C::BI / 8 / (C::NT / 64);   // 1 KB instructions per wavefront
+  //      straight into 1 KB of LDS (one 8-row slab), lane L landing at byte
+  //      16L. Lane L therefore fetches the global chunk that the swizzled
+  //      layout keeps at that spot: row 8n + L/8 of slab n, logical chunk
+  //      (L%8) ^ swz_key(row), where swz_key(row) = (L/8) ^ (n & 1). ----
+  constexpr int P_INSTR = C::BI / 8 / (C::NT / 64);   // slabs per wavefront
   constexpr int Q_INSTR = C::BJ / 8 / (C::NT / 64);
   static_assert(P_INSTR * 8 * (C::NT / 64) == C::BI && Q_INSTR * 8 * (C::NT / 64) == C::BJ, "tile rows per wave");
-  const int lrow = lane >> 3;                        // row within the 8-row slab
-  const int lchunk = (lane & 7) ^ lrow;              // logical chunk fetched by this lane
+  const int lrow = lane >> 3;
+  const uint32_t loff0 = (uint32_t)(lrow * p.K + (((lane & 7) ^ lrow) << 4));
+  const uint32_t loff1 = (uint32_t)(lrow * p.K + (((lane & 7) ^ lrow ^ 1) << 4));
   const uint8_t* pbase = p.P + (int64_t)i0 * p.K;
   const uint8_t* qbase = p.Q + (int64_t)j0 * p.K;
-  uint32_t poff[P_INSTR], qoff[Q_INSTR];
-#pragma unroll
-  for (int r = 0; r < P_INSTR; ++r) {
-    const int row = 8 * (wave * P_INSTR + r) + lrow;
-    poff[r] = (uint32_t)(min(row, p.I - 1 - i0) * p.K + lchunk * 16);
-  }
-#pragma unroll
-  for (int r = 0; r < Q_INSTR; ++r) {
-    const int row = 8 * (wave * Q_INSTR + r) + lrow;
-    qoff[r] = (uint32_t)(min(row, p.J - 1 - j0) * p.K + lchunk * 16);
-  }
-  // Scales: lanes of wavefronts 0.. fetch one float each into scales[st][0 .. SCALE_FLOATS).
-  const float* sg = nullptr;
-  int s_step = 0;
-  if (tid < C::BJ) {
-    sg = p.Qs + (int64_t)min(j0 + tid, p.J - 1) * p.Kb;
-    s_step = 1;
-  } else if (tid < C::BJ + C::PS_COUNT) {
-    const int k = tid - C::BJ;
-    if (PS_ROW) {
-      sg = p.Ps + (int64_t)min(i0 + k, p.I - 1) * p.Kb;
-      s_step = 1;
+  auto slab_src = [&](const uint8_t* base, int n, int rows, int kb) -> const uint8_t* {
+    const int s0 = 8 * n;
+    if (s0 + 8 <= rows) return base + (int64_t)s0 * p.K + ((n & 1) ? loff1 : loff0) + kb * 128;
+    const int row = min(s0 + lrow, rows - 1);
+    return base + (int64_t)row * p.K + (((lane & 7) ^ lrow ^ (n & 1)) << 4) + kb * 128;
+  };
+  // Scales. Thread t < ROWSC owns row t of the per-row scales (Q rows, then
+  // for WGrad the P rows) and fetches 4 consecutive K steps of it at once
+  // (one 16-byte load when K/128 is a multiple of 4), a group ahead. The last
+  // wavefront's first lanes fetch the block P scales each K step.
+  const bool vec4 = (p.Kb & 3) == 0;
+  const float* rsrc = nullptr;
+  if (tid < C::BJ)
+    rsrc = p.Qs + (int64_t)(j0 + min(tid, qrows - 1)) * p.Kb;
+  else if (PS_ROW && tid < C::ROWSC)
+    rsrc = p.Ps + (int64_t)(i0 + min(tid - C::BJ, prows - 1)) * p.Kb;
+  const int blk_lane = tid - (C::NT - 64);
+  const float* bsrc = nullptr;
+  if (!PS_ROW && blk_lane >= 0 && blk_lane < C::BLKSC)
+    bsrc = p.Ps + (int64_t)min((i0 / 128) + blk_lane, p.I / 128 - 1) * p.ps_ib;
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto load_row_scales = [&](int grp) {   // K steps 4grp .. 4grp+3 into rowsc[grp & 1]
+    if (!rsrc) return;
+    const int k0 = 4 * grp;
+    if (vec4) {
+      __builtin_amdgcn_global_load_lds(rsrc + k0, (lds_void*)(&rowsc[grp & 1][wave * 64 * 4]), 16, 0, 0);
     } else {
-      sg = p.Ps + (int64_t)min((i0 / 128) + k, p.I / 128 - 1) * p.ps_ib;
-      s_step = p.ps_kb;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rowsc[grp & 1][tid * 4 + q] = k0 + q < p.Kb ? rsrc[k0 + q] : 0.0f;
     }
-  }
+  };
   auto issue_loads = [&](int kb, int st) {
-    typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
-    for (int r = 0; r < P_INSTR; ++r)
-      __builtin_amdgcn_global_load_lds(pbase + poff[r] + kb * 128,
-                                       (lds_void*)(&tiles[st][(wave * P_INSTR + r) * 1024]), 16, 0, 0);
+    for (int r = 0; r < P_INSTR; ++r) {
+      const int n = wave * P_INSTR + r;
+      __builtin_amdgcn_global_load_lds(slab_src(pbase, n, prows, kb), (lds_void*)(&tiles[st][n * 1024]), 16, 0, 0);
+    }
 #pragma unroll
-    for (int r = 0; r < Q_INSTR; ++r)
-      __builtin_amdgcn_global_load_lds(qbase + qoff[r] + kb * 128,
-                                       (lds_void*)(&tiles[st][C::BI * 128 + (wave * Q_INSTR + r) * 1024]), 16, 0, 0);
-    if (sg) __builtin_amdgcn_global_load_lds(sg + (int64_t)kb * s_step, (lds_void*)(&scales[st][wave * 64]), 4, 0, 0);
+    for (int r = 0; r < Q_INSTR; ++r) {
+      const int n = wave * Q_INSTR + r;
+      __builtin_amdgcn_global_load_lds(slab_src(qbase, n, qrows, kb),
+                                       (lds_void*)(&tiles[st][C::BI * 128 + n * 1024]), 16, 0, 0);
+    }
+    if (bsrc) __builtin_amdgcn_global_load_lds(bsrc + (int64_t)kb * p.ps_kb, (lds_void*)(&blksc[st][0]), 4, 0, 0);
   };
 
   f32x4 acc[SI][SJ];
@@ -159,61 +182,112 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
     for (int b = 0; b < SJ; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   issue_loads(0, 0);
+  load_row_scales(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  // ---- main loop. Software pipeline over the SI row slices of the
+  //      wavefront tile: the MFMA of (slice a, column slice b) is issued right
+  //      before the FMAs that promote (slice a-1, column slice b), so the VALU
+  //      promotion of one slice runs while the matrix core works on the next.
+  //      The last slice of a K step is promoted at the start of the next K
+  //      step (at the first step the carried partials and scales are zero). ----
   const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto load_frag = [&](const uint8_t* t, int row) -> i32x8 {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(t + swz(row, 2 * g));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(t + swz(row, 2 * g + 1));
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  // promote one 16x16 partial: acc += d * (row scale) * (column scale)
+  auto promote1 = [&](f32x4& accv, const f32x4& d, float cs, const f32x4& rs) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (PS_ROW)
+        accv[r] = __builtin_fmaf(d[r], rs[r] * cs, accv[r]);
+      else
+        accv[r] = __builtin_fmaf(d[r], cs, accv[r]);
+    }
+  };
+  constexpr int PROMOTE_VALU = PS_ROW ? 8 : 4;
+  // Block-scaled roles carry the last slice's promotion into the next K step;
+  // the row-scaled role (twice the promotion VALU and registers) promotes it
+  // at the end of its own step.
+  constexpr bool CARRY = !PS_ROW;
+
+  f32x4 dprev[SJ];
+  float ccarry[SJ];
+#pragma unroll
+  for (int b = 0; b < SJ; ++b) {
+    dprev[b] = zero;
+    ccarry[b] = 0.0f;
+  }
+  f32x4 rprev = zero;
   for (int kb = 0; kb < p.Kb; ++kb) {
     const int st = kb & 1;
-    if (kb + 1 < p.Kb) issue_loads(kb + 1, st ^ 1);
-
     const uint8_t* tp = tiles[st];
     const uint8_t* tq = tiles[st] + C::BI * 128;
-    const float* sq = scales[st];
-    const float* sp = scales[st] + C::BJ;
+    const float* rsc = &rowsc[(kb >> 2) & 1][kb & 3];   // scale of row r at rsc[4 r]
 
     i32x8 qf[SJ];
-    float qsc[SJ];
+    float cj[SJ];
 #pragma unroll
     for (int b = 0; b < SJ; ++b) {
       const int row = wj * C::WJ + b * 16 + r16;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(tq + swz(row, 2 * g));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(tq + swz(row, 2 * g + 1));
-      qf[b] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      qsc[b] = sq[row];
+      qf[b] = load_frag(tq, row);
+      cj[b] = rsc[4 * row];
     }
-    float cj[SJ];
     if (!PS_ROW) {
-      const float psw = sp[(wi * C::WI) / 128];
+      const float psw = blksc[st][(wi * C::WI) / 128];
 #pragma unroll
-      for (int b = 0; b < SJ; ++b) cj[b] = qsc[b] * psw;
+      for (int b = 0; b < SJ; ++b) cj[b] *= psw;
     }
+    // the next group of row scales goes out at the first step of each group
+    if ((kb & 3) == 0 && kb + 4 < p.Kb) load_row_scales((kb >> 2) + 1);
 
+    // next stage's loads go out after this step's first LDS reads
+    if (kb + 1 < p.Kb) issue_loads(kb + 1, st ^ 1);
 #pragma unroll
     for (int a = 0; a < SI; ++a) {
-      const int row = wi * C::WI + a * 16 + r16;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(tp + swz(row, 2 * g));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(tp + swz(row, 2 * g + 1));
-      const i32x8 pf = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      f32x4 ps4;
-      if (PS_ROW) ps4 = *reinterpret_cast<const f32x4*>(sp + wi * C::WI + a * 16 + 4 * g);
+      const i32x8 pf = load_frag(tp, wi * C::WI + a * 16 + r16);
+      f32x4 rs = zero;
+      if (PS_ROW) {
+        const int prow = C::BJ + wi * C::WI + a * 16 + 4 * g;
+        rs = f32x4{rsc[4 * prow], rsc[4 * prow + 4], rsc[4 * prow + 8], rsc[4 * prow + 12]};
+      }
 #pragma unroll
       for (int b = 0; b < SJ; ++b) {
-        const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pf, qf[b], zero, 0, 0, 0, 0, 0, 0);
-        if (PS_ROW) {
+        const f32x4 dcur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pf, qf[b], zero, 0, 0, 0, 0, 0, 0);
+        if (a > 0)
+          promote1(acc[a - 1][b], dprev[b], cj[b], rprev);
+        else if (CARRY)
+          promote1(acc[SI - 1][b], dprev[b], ccarry[b], rprev);
+        dprev[b] = dcur;
+      }
+      // one MFMA, then the promotion of the partial it replaced, in turn
+      // (the row-scaled role schedules better left to the compiler)
+      if (!PS_ROW) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[a][b][r] = __builtin_fmaf(d[r], ps4[r] * qsc[b], acc[a][b][r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[a][b][r] = __builtin_fmaf(d[r], cj[b], acc[a][b][r]);
+        for (int b = 0; b < SJ; ++b) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, PROMOTE_VALU, 0);
         }
       }
+      rprev = rs;
+    }
+    if (CARRY) {
+#pragma unroll
+      for (int b = 0; b < SJ; ++b) ccarry[b] = cj[b];
+    } else {
+#pragma unroll
+      for (int b = 0; b < SJ; ++b) promote1(acc[SI - 1][b], dprev[b], cj[b], rprev);
     }
 
     __builtin_amdgcn_s_waitcnt(0);   // this thread's loads into the other stage have landed
     __syncthreads();
+  }
+  if (CARRY) {
+#pragma unroll
+    for (int b = 0; b < SJ; ++b) promote1(acc[SI - 1][b], dprev[b], ccarry[b], rprev);
   }
 
   // ---- epilogue: lane holds out[j][i .. i+3] for each (a, b) ----

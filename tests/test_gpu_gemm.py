@@ -51,11 +51,24 @@ def _assert_bits_equal(out_bits, want_bits, ref, what):
 GRIDS = {"narrow": inputs.NARROW_GRID, "wide": None}
 
 
-def _check_exact_or_close(out_bits, ref, grid, what):
+def _check_exact_or_close(out_bits, ref, grid, what, amax_prod):
+    """Narrow grid: bit-exact. Wide grid: within the MFMA's own error bound.
+
+    The wide grid puts a 448 x 448 product in every 128-long block of every
+    output and lets it cancel against the rest, which stresses the matrix
+    core's internal accumulation. Measured on gfx950, one fp8 16x16x128 dot
+    product deviates from the exact sum by at most ~2^-11.8 of its largest
+    product; the bound used here is 2^-10 of the largest possible product per
+    block (amax_x * amax_w = 448^2 * sx * sw, summed over blocks) plus the
+    bf16 rounding of the result.
+    """
     if grid == "narrow":
         _assert_bits_equal(out_bits, gemm.bf16_rne(ref), ref, f"exact {what}")
-    else:
-        _assert_close(out_bits, ref, f"wide-grid {what}")
+        return
+    got = gemm.bf16_bits_to_f64(out_bits)
+    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -10 * amax_prod
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), f"wide-grid {what}: {bad.sum()} outputs beyond the MFMA bound"
 
 
 @pytest.mark.parametrize("grid", list(GRIDS))
@@ -72,7 +85,7 @@ def test_exact_fwd(grid):
     oxq, oxs = quant.quantize_act_1x128(x)
     owq, ows, _ = quant.quantize_weight_128x128(w)
     ref = gemm.gemm_fwd(oxq, oxs, owq, ows)
-    _check_exact_or_close(host_bits(y), ref, grid, "fwd")
+    _check_exact_or_close(host_bits(y), ref, grid, "fwd", 448.0 ** 2 * (oxs.astype(np.float64) @ ows.astype(np.float64).repeat(128, axis=0).T))
 
 
 @pytest.mark.parametrize("grid", list(GRIDS))
@@ -89,7 +102,7 @@ def test_exact_dgrad(grid):
     odq, ods = quant.quantize_act_1x128(dy)
     owq, ows, _ = quant.quantize_weight_128x128(w)
     ref = gemm.gemm_dgrad(odq, ods, owq, ows)
-    _check_exact_or_close(host_bits(dx), ref, grid, "dgrad")
+    _check_exact_or_close(host_bits(dx), ref, grid, "dgrad", 448.0 ** 2 * (ods.astype(np.float64) @ ows.astype(np.float64).repeat(128, axis=1)))
 
 
 @pytest.mark.parametrize("grid", list(GRIDS))
@@ -106,7 +119,7 @@ def test_exact_wgrad(grid):
     oq1, os1 = quant.transpose_quantize_128x1(dy)
     oq2, os2 = quant.transpose_quantize_128x1(x)
     ref = gemm.gemm_wgrad(oq1, os1, oq2, os2)
-    _check_exact_or_close(host_bits(dw), ref, grid, "wgrad")
+    _check_exact_or_close(host_bits(dw), ref, grid, "wgrad", 448.0 ** 2 * (os1.astype(np.float64) @ os2.astype(np.float64).T))
 
 
 # ------------------------------------------- oracle operands, small shapes --
