@@ -64,8 +64,9 @@ __device__ __forceinline__ void map_tile(int bid, int nblk, int tiles_i, int til
   tj = in_group / gsize;
 }
 
-template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW>
+template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST_ = 2>
 struct GemmCfg {
+  static constexpr int NST = NST_;                               // LDS stages (K steps in flight + 1)
   static constexpr int WI = SI * 16, WJ = SJ * 16;              // wavefront tile
   static constexpr int BI = WAVES_I * WI, BJ = WAVES_J * WJ;    // workgroup tile
   static constexpr int NT = 64 * WAVES_I * WAVES_J;
@@ -75,7 +76,8 @@ struct GemmCfg {
   static constexpr int BLKSC = PS_ROW ? 0 : BI / 128;            // 128x128-block P scales per K step
   static constexpr int TILE_BYTES = (BI + BJ) * 128;
   static_assert(BI * 8 % NT == 0 && BJ * 8 % NT == 0, "loads must divide evenly");
-  static_assert(NT >= ROWSC && BLKSC <= 64, "one scale load per thread at most");
+  static constexpr int ROW_PASSES = (ROWSC + NT - 1) / NT;      // per-row scales per thread
+  static_assert(BLKSC <= 64 && BJ % 64 == 0 && NT % 64 == 0, "scale lanes");
   static_assert(PS_ROW || (128 % WI == 0), "a block-scaled wavefront must sit inside one 128-row block");
   static_assert(BI % 128 == 0, "BI must be a multiple of 128");
 };
@@ -90,18 +92,49 @@ struct GemmCfg {
 __device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_key(row)) << 4); }
 
-template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW>
+// Asynchronous global -> LDS copies ("LDS DMA"): every lane of the wavefront
+// sends SIZE bytes from (sbase + voff) to LDS at lds + SIZE * lane. sbase and
+// lds are wavefront-uniform (SGPR / M0), voff is a per-lane 32-bit offset.
+// Written as inline assembly so the compiler neither keeps 64-bit per-lane
+// pointers live nor inserts waits for these copies before unrelated LDS
+// reads; the kernel waits for them itself (a vmcnt wait before each barrier).
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ uint64_t uniform_ptr(const void* ptr) {
+  const uint64_t v = (uint64_t)(uintptr_t)ptr;
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* lds) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void*)lds);
+}
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(uniform_ptr(sbase)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(uniform_ptr(sbase)) : "memory", "m0");
+}
+// Wait until at most N vector-memory operations of this wavefront are in
+// flight (they complete in order), leaving LDS and export counters alone.
+template <int N>
+__device__ __forceinline__ void wait_dma_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
 __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses LDS address-space casts, device pass only
-  using C = GemmCfg<WAVES_I, WAVES_J, SI, SJ, PS_ROW>;
-  __shared__ __align__(16) uint8_t tiles[2][C::TILE_BYTES];
+  using C = GemmCfg<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST>;
+  __shared__ __align__(16) uint8_t tiles[NST][C::TILE_BYTES];
   // Per-row scales come in groups of 4 K steps, [row][4], double-buffered by
   // group; block P scales come per K step.
   __shared__ __align__(16) float rowsc[2][C::ROWSC * 4];
-  __shared__ __align__(16) float blksc[2][C::BLKSC > 0 ? C::BLKSC : 1];
+  __shared__ __align__(16) float blksc[NST][C::BLKSC > 0 ? C::BLKSC : 1];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wi = wave % WAVES_I, wj = wave / WAVES_I;
   const int g = lane >> 4, r16 = lane & 15;
 
@@ -109,18 +142,17 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
   map_tile(blockIdx.x, gridDim.x, p.tiles_i, p.tiles_j, ti, tj);
   // The last tile along a dimension is shifted back to end at the edge, so
   // every row it loads exists; where it overlaps its neighbour both compute
-  // and store the same values. Only a dimension smaller than one tile needs
-  // clamped rows (their outputs are never stored).
+  // and store the same values. Only a dimension smaller than one tile (the
+  // CLAMP instantiation) needs clamped rows, whose outputs are never stored.
   const int i0 = p.I >= C::BI ? min(ti * C::BI, p.I - C::BI) : 0;
   const int j0 = p.J >= C::BJ ? min(tj * C::BJ, p.J - C::BJ) : 0;
   const int prows = min(p.I - i0, C::BI);
   const int qrows = min(p.J - j0, C::BJ);
 
-  // ---- global -> LDS loads. Each wavefront instruction moves 64 x 16 bytes
-  //      straight into 1 KB of LDS (one 8-row slab), lane L landing at byte
-  //      16L. Lane L therefore fetches the global chunk that the swizzled
-  //      layout keeps at that spot: row 8n + L/8 of slab n, logical chunk
-  //      (L%8) ^ swz_key(row), where swz_key(row) = (L/8) ^ (n & 1). ----
+  // ---- operand tiles. One DMA instruction moves one 8-row slab (1 KB), lane
+  //      L landing at byte 16L. Lane L therefore fetches the global chunk that
+  //      the swizzled layout keeps at that spot: row 8n + L/8 of slab n,
+  //      logical chunk (L%8) ^ swz_key(row), where swz_key(row) = (L/8) ^ (n & 1). ----
   constexpr int P_INSTR = C::BI / 8 / (C::NT / 64);   // slabs per wavefront
   constexpr int Q_INSTR = C::BJ / 8 / (C::NT / 64);
   static_assert(P_INSTR * 8 * (C::NT / 64) == C::BI && Q_INSTR * 8 * (C::NT / 64) == C::BJ, "tile rows per wave");
@@ -129,50 +161,49 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
   const uint32_t loff1 = (uint32_t)(lrow * p.K + (((lane & 7) ^ lrow ^ 1) << 4));
   const uint8_t* pbase = p.P + (int64_t)i0 * p.K;
   const uint8_t* qbase = p.Q + (int64_t)j0 * p.K;
-  auto slab_src = [&](const uint8_t* base, int n, int rows, int kb) -> const uint8_t* {
-    const int s0 = 8 * n;
-    if (s0 + 8 <= rows) return base + (int64_t)s0 * p.K + ((n & 1) ? loff1 : loff0) + kb * 128;
-    const int row = min(s0 + lrow, rows - 1);
-    return base + (int64_t)row * p.K + (((lane & 7) ^ lrow ^ (n & 1)) << 4) + kb * 128;
-  };
-  // Scales. Thread t < ROWSC owns row t of the per-row scales (Q rows, then
-  // for WGrad the P rows) and fetches 4 consecutive K steps of it at once
-  // (one 16-byte load when K/128 is a multiple of 4), a group ahead. The last
-  // wavefront's first lanes fetch the block P scales each K step.
-  const bool vec4 = (p.Kb & 3) == 0;
-  const float* rsrc = nullptr;
-  if (tid < C::BJ)
-    rsrc = p.Qs + (int64_t)(j0 + min(tid, qrows - 1)) * p.Kb;
-  else if (PS_ROW && tid < C::ROWSC)
-    rsrc = p.Ps + (int64_t)(i0 + min(tid - C::BJ, prows - 1)) * p.Kb;
-  const int blk_lane = tid - (C::NT - 64);
-  const float* bsrc = nullptr;
-  if (!PS_ROW && blk_lane >= 0 && blk_lane < C::BLKSC)
-    bsrc = p.Ps + (int64_t)min((i0 / 128) + blk_lane, p.I / 128 - 1) * p.ps_ib;
-  typedef __attribute__((address_space(3))) void lds_void;
-  auto load_row_scales = [&](int grp) {   // K steps 4grp .. 4grp+3 into rowsc[grp & 1]
-    if (!rsrc) return;
-    const int k0 = 4 * grp;
-    if (vec4) {
-      __builtin_amdgcn_global_load_lds(rsrc + k0, (lds_void*)(&rowsc[grp & 1][wave * 64 * 4]), 16, 0, 0);
+  auto slab = [&](const uint8_t* base, int n, int rows, int kb, const void* ldst) {
+    if (!CLAMP) {
+      dma16(base + (int64_t)(8 * n) * p.K + kb * 128, (n & 1) ? loff1 : loff0, ldst);
     } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) rowsc[grp & 1][tid * 4 + q] = k0 + q < p.Kb ? rsrc[k0 + q] : 0.0f;
+      const int row = min(8 * n + lrow, rows - 1);
+      dma16(base + kb * 128, (uint32_t)(row * p.K + (((lane & 7) ^ lrow ^ (n & 1)) << 4)), ldst);
     }
   };
-  auto issue_loads = [&](int kb, int st) {
+  auto p_slab = [&](int r, int kb, int st) { slab(pbase, wave * P_INSTR + r, prows, kb, &tiles[st][(wave * P_INSTR + r) * 1024]); };
+  auto q_slab = [&](int r, int kb, int st) {
+    slab(qbase, wave * Q_INSTR + r, qrows, kb, &tiles[st][C::BI * 128 + (wave * Q_INSTR + r) * 1024]);
+  };
+
+  // ---- scales. Thread t < ROWSC owns row t of the per-row scales (Q rows,
+  //      then for WGrad the P rows) and fetches 4 consecutive K steps of it
+  //      at once (one 16-byte copy when K/128 is a multiple of 4), a group
+  //      ahead. The last wavefront's first lanes fetch the block P scales
+  //      each K step. ----
+  const bool vec4 = (p.Kb & 3) == 0;
+  auto load_row_scales = [&](int grp) {   // K steps 4grp .. 4grp+3 into rowsc[grp & 1]
 #pragma unroll
-    for (int r = 0; r < P_INSTR; ++r) {
-      const int n = wave * P_INSTR + r;
-      __builtin_amdgcn_global_load_lds(slab_src(pbase, n, prows, kb), (lds_void*)(&tiles[st][n * 1024]), 16, 0, 0);
-    }
+    for (int pass = 0; pass < C::ROW_PASSES; ++pass) {
+      const int r = tid + pass * C::NT;                   // scale row owned by this lane
+      const int rw = wave * 64 + pass * C::NT;            // first row of this wavefront (uniform)
+      if (rw >= C::ROWSC) continue;
+      const bool q_rows = rw < C::BJ;                     // the 64 rows are all Q or all P rows
+      const float* rbase = q_rows ? p.Qs + (int64_t)j0 * p.Kb : p.Ps + (int64_t)i0 * p.Kb;
+      const int rrow = q_rows ? min(r, qrows - 1) : min(r - C::BJ, prows - 1);
+      const int k0 = 4 * grp;
+      if (vec4) {
+        dma16(rbase, (uint32_t)((rrow * p.Kb + k0) * 4), &rowsc[grp & 1][rw * 4]);
+      } else {
+        const float* src = rbase + (int64_t)rrow * p.Kb;
 #pragma unroll
-    for (int r = 0; r < Q_INSTR; ++r) {
-      const int n = wave * Q_INSTR + r;
-      __builtin_amdgcn_global_load_lds(slab_src(qbase, n, qrows, kb),
-                                       (lds_void*)(&tiles[st][C::BI * 128 + n * 1024]), 16, 0, 0);
+        for (int q = 0; q < 4; ++q) rowsc[grp & 1][r * 4 + q] = k0 + q < p.Kb ? src[k0 + q] : 0.0f;
+      }
     }
-    if (bsrc) __builtin_amdgcn_global_load_lds(bsrc + (int64_t)kb * p.ps_kb, (lds_void*)(&blksc[st][0]), 4, 0, 0);
+  };
+  const int blk_lane = tid - (C::NT - 64);
+  const bool bl = !PS_ROW && blk_lane >= 0 && blk_lane < C::BLKSC;
+  const int bblk = min((i0 / 128) + max(blk_lane, 0), p.I / 128 - 1);
+  auto load_blk_scales = [&](int kb, int st) {
+    if (bl) dma4(p.Ps, (uint32_t)((bblk * p.ps_ib + kb * p.ps_kb) * 4), &blksc[st][0]);
   };
 
   f32x4 acc[SI][SJ];
@@ -181,9 +212,19 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
 #pragma unroll
     for (int b = 0; b < SJ; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  issue_loads(0, 0);
+  // Prologue: scales, then the first NST-1 stages (oldest first).
+  constexpr int SLABS = P_INSTR + Q_INSTR;   // copies per wavefront per stage
   load_row_scales(0);
-  __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+  for (int s0 = 0; s0 < NST - 1; ++s0) load_blk_scales(min(s0, p.Kb - 1), s0);
+#pragma unroll
+  for (int s0 = 0; s0 < NST - 1; ++s0) {
+#pragma unroll
+    for (int r = 0; r < P_INSTR; ++r) p_slab(r, min(s0, p.Kb - 1), s0);
+#pragma unroll
+    for (int r = 0; r < Q_INSTR; ++r) q_slab(r, min(s0, p.Kb - 1), s0);
+  }
+  wait_dma_keep<(NST - 2) * SLABS>();        // stage 0 (and every scale) has landed
   __syncthreads();
 
   // ---- main loop. Software pipeline over the SI row slices of the
@@ -222,12 +263,15 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
     ccarry[b] = 0.0f;
   }
   f32x4 rprev = zero;
+  int st = 0;                       // stage of step kb
   for (int kb = 0; kb < p.Kb; ++kb) {
-    const int st = kb & 1;
     const uint8_t* tp = tiles[st];
     const uint8_t* tq = tiles[st] + C::BI * 128;
     const float* rsc = &rowsc[(kb >> 2) & 1][kb & 3];   // scale of row r at rsc[4 r]
 
+    // First P fragment, then the Q fragments in the order the first slice
+    // uses them, so its first MFMA waits for two fragments only.
+    i32x8 pf0 = load_frag(tp, wi * C::WI + r16);
     i32x8 qf[SJ];
     float cj[SJ];
 #pragma unroll
@@ -244,11 +288,23 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
     // the next group of row scales goes out at the first step of each group
     if ((kb & 3) == 0 && kb + 4 < p.Kb) load_row_scales((kb >> 2) + 1);
 
-    // next stage's loads go out after this step's first LDS reads
-    if (kb + 1 < p.Kb) issue_loads(kb + 1, st ^ 1);
+    // The next stage's tiles go out spread over the first slices (a few
+    // copies at a time keep the memory pipeline from stalling the wavefront);
+    // at the last step they re-fetch the last stage into the idle buffer.
+    const int kn = min(kb + NST - 1, p.Kb - 1);
+    const int sn = st == 0 ? NST - 1 : st - 1;    // stage of step kb + NST - 1 (idle now)
+    load_blk_scales(kn, sn);
+    constexpr int LOAD_SLICES = 4;
+    static_assert(P_INSTR % LOAD_SLICES == 0 && Q_INSTR % LOAD_SLICES == 0 && SI >= LOAD_SLICES, "load spread");
 #pragma unroll
     for (int a = 0; a < SI; ++a) {
-      const i32x8 pf = load_frag(tp, wi * C::WI + a * 16 + r16);
+      if (a < LOAD_SLICES) {
+#pragma unroll
+        for (int r = 0; r < P_INSTR / LOAD_SLICES; ++r) p_slab(a * (P_INSTR / LOAD_SLICES) + r, kn, sn);
+#pragma unroll
+        for (int r = 0; r < Q_INSTR / LOAD_SLICES; ++r) q_slab(a * (Q_INSTR / LOAD_SLICES) + r, kn, sn);
+      }
+      const i32x8 pf = a == 0 ? pf0 : load_frag(tp, wi * C::WI + a * 16 + r16);
       f32x4 rs = zero;
       if (PS_ROW) {
         const int prow = C::BJ + wi * C::WI + a * 16 + 4 * g;
@@ -282,13 +338,17 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
       for (int b = 0; b < SJ; ++b) promote1(acc[SI - 1][b], dprev[b], cj[b], rprev);
     }
 
-    __builtin_amdgcn_s_waitcnt(0);   // this thread's loads into the other stage have landed
+    // the copies for step kb+1 (issued NST-2 steps ago) have landed; this
+    // step's copies may stay in flight when NST > 2
+    wait_dma_keep<(NST - 2) * SLABS>();
     __syncthreads();
+    st = st + 1 == NST ? 0 : st + 1;
   }
   if (CARRY) {
 #pragma unroll
     for (int b = 0; b < SJ; ++b) promote1(acc[SI - 1][b], dprev[b], ccarry[b], rprev);
   }
+  wait_dma_keep<0>();   // no copy into LDS may outlive the workgroup
 
   // ---- epilogue: lane holds out[j][i .. i+3] for each (a, b) ----
 #pragma unroll
@@ -307,19 +367,30 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
 }
 
 // ----------------------------------------------------------------------------
-// Tile configurations. The large one keeps two wavefronts per SIMD (512
-// threads, 256 x 256 output per workgroup, 128 x 64 per wavefront).
+// Launch one configuration: the CLAMP instantiation only where a dimension is
+// smaller than one tile.
 // ----------------------------------------------------------------------------
-template <bool PS_ROW>
-static hipError_t run_gemm(GemmParams p, hipStream_t stream) {
-  constexpr int WAVES_I = 2, WAVES_J = 4, SI = 8, SJ = 4;
-  using C = GemmCfg<WAVES_I, WAVES_J, SI, SJ, PS_ROW>;
+template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST>
+static hipError_t run_gemm_cfg(GemmParams p, hipStream_t stream) {
+  using C = GemmCfg<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST>;
   p.tiles_i = (p.I + C::BI - 1) / C::BI;
   p.tiles_j = (p.J + C::BJ - 1) / C::BJ;
   const int nblk = p.tiles_i * p.tiles_j;
-  hipLaunchKernelGGL((fp8_gemm_kernel<WAVES_I, WAVES_J, SI, SJ, PS_ROW>), dim3(nblk), dim3(C::NT), 0,
-                     stream, p);
+  if (p.I >= C::BI && p.J >= C::BJ)
+    hipLaunchKernelGGL((fp8_gemm_kernel<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, false>), dim3(nblk), dim3(C::NT), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((fp8_gemm_kernel<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, true>), dim3(nblk), dim3(C::NT), 0,
+                       stream, p);
   return hipGetLastError();
+}
+
+// 256 x 256 tile, 8 wavefronts (2 per SIMD) of 128 x 64, 2 LDS stages. (A
+// 256 x 128 tile with one wavefront per SIMD and 3 stages measured slower:
+// one wavefront cannot hide its own LDS fragment latency.)
+template <bool PS_ROW>
+static hipError_t run_gemm(GemmParams p, hipStream_t stream) {
+  return run_gemm_cfg<2, 4, 8, 4, PS_ROW, 2>(p, stream);
 }
 
 hipError_t launch_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
