@@ -12,6 +12,7 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;   // every dimension < 2^31
 constexpr int64_t kMaxElems = (int64_t)1 << 40;  // every tensor < 2^40 elements
+constexpr int64_t kMaxContraction = (int64_t)1 << 24;  // GEMM contraction length < 2^24
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
@@ -70,7 +71,7 @@ int transpose_quantize_128x1(const void* x, int64_t M, int64_t C, uint8_t* xq_t,
 
 int fp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
                  int64_t M, int64_t N, int64_t K, void* stream) {
-  if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N) || N % 128 || K % 128)
+  if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N) || N % 128 || K % 128 || K >= kMaxContraction)
     return FP8BSQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BSQ_OK;
   if (K == 0) return FP8BSQ_ERR_SHAPE;  // an empty contraction would leave y unwritten
@@ -82,7 +83,7 @@ int fp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const fl
 
 int fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
                    void* dx, int64_t M, int64_t N, int64_t K, void* stream) {
-  if (!dims_ok(M, N) || !dims_ok(K, N) || !dims_ok(M, K) || N % 128 || K % 128)
+  if (!dims_ok(M, N) || !dims_ok(K, N) || !dims_ok(M, K) || N % 128 || K % 128 || N >= kMaxContraction)
     return FP8BSQ_ERR_SHAPE;
   if (M == 0 || K == 0) return FP8BSQ_OK;
   if (N == 0) return FP8BSQ_ERR_SHAPE;
@@ -94,7 +95,8 @@ int fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, co
 
 int fp8_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t, const float* xs_t,
                    void* dw, int64_t M, int64_t N, int64_t K, void* stream) {
-  if (!dims_ok(N, M) || !dims_ok(K, M) || !dims_ok(N, K) || M % 128 || N % 128 || K % 128)
+  if (!dims_ok(N, M) || !dims_ok(K, M) || !dims_ok(N, K) || M % 128 || N % 128 || K % 128 ||
+      M >= kMaxContraction)
     return FP8BSQ_ERR_SHAPE;
   if (N == 0 || K == 0) return FP8BSQ_OK;
   if (M == 0) return FP8BSQ_ERR_SHAPE;

@@ -74,6 +74,7 @@ struct GemmCfg {
   static constexpr int Q_LOADS = BJ * 8 / NT;
   static constexpr int ROWSC = BJ + (PS_ROW ? BI : 0);          // per-row scales per K step
   static constexpr int BLKSC = PS_ROW ? 0 : BI / 128;            // 128x128-block P scales per K step
+  static constexpr int BLKSC_PAD = BLKSC > 0 ? BLKSC : 1;
   static constexpr int TILE_BYTES = (BI + BJ) * 128;
   static_assert(BI * 8 % NT == 0 && BJ * 8 % NT == 0, "loads must divide evenly");
   static constexpr int ROW_PASSES = (ROWSC + NT - 1) / NT;      // per-row scales per thread
@@ -93,27 +94,29 @@ __device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3)
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_key(row)) << 4); }
 
 // Asynchronous global -> LDS copies ("LDS DMA"): every lane of the wavefront
-// sends SIZE bytes from (sbase + voff) to LDS at lds + SIZE * lane. sbase and
-// lds are wavefront-uniform (SGPR / M0), voff is a per-lane 32-bit offset.
-// Written as inline assembly so the compiler neither keeps 64-bit per-lane
-// pointers live nor inserts waits for these copies before unrelated LDS
-// reads; the kernel waits for them itself (a vmcnt wait before each barrier).
+// sends SIZE bytes from (sbase + voff) to LDS byte address lds + SIZE * lane.
+// sbase and lds are wavefront-uniform (SGPR pair / M0), voff is a per-lane
+// 32-bit offset. Written as inline assembly so the compiler neither keeps
+// 64-bit per-lane pointers live nor inserts waits for these copies before
+// unrelated LDS reads; the kernel waits for them itself (a vmcnt wait before
+// each barrier). The s_nop is the wait state a copy needs after M0 is written.
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ uint64_t uniform_ptr(const void* ptr) {
   const uint64_t v = (uint64_t)(uintptr_t)ptr;
   return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
 }
+// LDS byte address of a __shared__ object (wavefront-uniform).
 __device__ __forceinline__ uint32_t lds_addr(const void* lds) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void*)lds);
 }
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds_addr(lds)), "v"(voff), "s"(uniform_ptr(sbase)) : "memory", "m0");
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(uniform_ptr(sbase)) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, const void* lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
-               :: "s"(lds_addr(lds)), "v"(voff), "s"(uniform_ptr(sbase)) : "memory", "m0");
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds), "v"(voff), "s"(uniform_ptr(sbase)) : "memory", "m0");
 }
 // Wait until at most N vector-memory operations of this wavefront are in
 // flight (they complete in order), leaving LDS and export counters alone.
@@ -131,7 +134,18 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
   // Per-row scales come in groups of 4 K steps, [row][4], double-buffered by
   // group; block P scales come per K step.
   __shared__ __align__(16) float rowsc[2][C::ROWSC * 4];
-  __shared__ __align__(16) float blksc[NST][C::BLKSC > 0 ? C::BLKSC : 1];
+  __shared__ __align__(16) float blksc[NST][C::BLKSC_PAD];
+  // The block-scaled roles (X W^T, dY W) prefetch each K step's tile rows
+  // into L2 one step before their LDS copies go out; for the row-scaled role
+  // (dY^T X, rows a full token count apart) this measured slower.
+  constexpr bool PF_L2 = !PS_ROW;
+  // Landing area of the L2 prefetch copies (never read).
+  __shared__ __align__(16) uint32_t pf_sink[PF_L2 ? C::NT : 1];
+
+  const uint32_t tiles_lds = lds_addr(&tiles[0][0]);
+  const uint32_t rowsc_lds = lds_addr(&rowsc[0][0]);
+  const uint32_t blksc_lds = lds_addr(&blksc[0][0]);
+  const uint32_t sink_lds = lds_addr(&pf_sink[0]);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -161,18 +175,33 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
   const uint32_t loff1 = (uint32_t)(lrow * p.K + (((lane & 7) ^ lrow ^ 1) << 4));
   const uint8_t* pbase = p.P + (int64_t)i0 * p.K;
   const uint8_t* qbase = p.Q + (int64_t)j0 * p.K;
-  auto slab = [&](const uint8_t* base, int n, int rows, int kb, const void* ldst) {
+  auto slab = [&](const uint8_t* base, int n, int rows, int kb, uint32_t ldst) {
     if (!CLAMP) {
       dma16(base + (int64_t)(8 * n) * p.K + kb * 128, (n & 1) ? loff1 : loff0, ldst);
     } else {
       const int row = min(8 * n + lrow, rows - 1);
-      dma16(base + kb * 128, (uint32_t)(row * p.K + (((lane & 7) ^ lrow ^ (n & 1)) << 4)), ldst);
+      dma16(base + kb * 128, (uint32_t)row * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ lrow ^ (n & 1)) << 4), ldst);
     }
   };
-  auto p_slab = [&](int r, int kb, int st) { slab(pbase, wave * P_INSTR + r, prows, kb, &tiles[st][(wave * P_INSTR + r) * 1024]); };
-  auto q_slab = [&](int r, int kb, int st) {
-    slab(qbase, wave * Q_INSTR + r, qrows, kb, &tiles[st][C::BI * 128 + (wave * Q_INSTR + r) * 1024]);
+  auto p_slab = [&](int r, int kb, int st) {
+    slab(pbase, wave * P_INSTR + r, prows, kb, tiles_lds + st * C::TILE_BYTES + (wave * P_INSTR + r) * 1024);
   };
+  auto q_slab = [&](int r, int kb, int st) {
+    slab(qbase, wave * Q_INSTR + r, qrows, kb,
+         tiles_lds + st * C::TILE_BYTES + C::BI * 128 + (wave * Q_INSTR + r) * 1024);
+  };
+
+  // ---- L2 prefetch: each lane touches the 128-byte segment of one tile row
+  //      for K step kb (P rows then Q rows, one row per lane), so that the LDS
+  //      copies of that step, issued a step later, hit in L2. The 4-byte copy
+  //      lands in pf_sink. ----
+  static_assert(!PF_L2 || C::BI + C::BJ == C::NT, "one prefetch row per lane");
+  const bool pf_p = wave * 64 < C::BI;                        // wavefront-uniform
+  const uint8_t* pf_base = pf_p ? pbase + (int64_t)(CLAMP ? 0 : wave * 64) * p.K
+                                : qbase + (int64_t)(CLAMP ? 0 : wave * 64 - C::BI) * p.K;
+  const uint32_t pf_off = CLAMP ? (uint32_t)(pf_p ? min(wave * 64 + lane, prows - 1) : min(wave * 64 - C::BI + lane, qrows - 1)) * (uint32_t)p.K
+                                : (uint32_t)lane * (uint32_t)p.K;
+  auto prefetch = [&](int kb) { dma4(pf_base + kb * 128, pf_off, sink_lds + wave * 256); };
 
   // ---- scales. Thread t < ROWSC owns row t of the per-row scales (Q rows,
   //      then for WGrad the P rows) and fetches 4 consecutive K steps of it
@@ -191,7 +220,7 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
       const int rrow = q_rows ? min(r, qrows - 1) : min(r - C::BJ, prows - 1);
       const int k0 = 4 * grp;
       if (vec4) {
-        dma16(rbase, (uint32_t)((rrow * p.Kb + k0) * 4), &rowsc[grp & 1][rw * 4]);
+        dma16(rbase, (uint32_t)((rrow * p.Kb + k0) * 4), rowsc_lds + ((grp & 1) * C::ROWSC + rw) * 16);
       } else {
         const float* src = rbase + (int64_t)rrow * p.Kb;
 #pragma unroll
@@ -203,7 +232,7 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
   const bool bl = !PS_ROW && blk_lane >= 0 && blk_lane < C::BLKSC;
   const int bblk = min((i0 / 128) + max(blk_lane, 0), p.I / 128 - 1);
   auto load_blk_scales = [&](int kb, int st) {
-    if (bl) dma4(p.Ps, (uint32_t)((bblk * p.ps_ib + kb * p.ps_kb) * 4), &blksc[st][0]);
+    if (bl) dma4(p.Ps, (uint32_t)((bblk * p.ps_ib + kb * p.ps_kb) * 4), blksc_lds + st * C::BLKSC_PAD * 4);
   };
 
   f32x4 acc[SI][SJ];
@@ -340,7 +369,8 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
 
     // the copies for step kb+1 (issued NST-2 steps ago) have landed; this
     // step's copies may stay in flight when NST > 2
-    wait_dma_keep<(NST - 2) * SLABS>();
+    if (PF_L2) prefetch(min(kb + NST, p.Kb - 1));
+    wait_dma_keep<(NST - 2) * SLABS + (PF_L2 ? 1 : 0)>();
     __syncthreads();
     st = st + 1 == NST ? 0 : st + 1;
   }

@@ -34,8 +34,9 @@
  *     validated before any HIP runtime call, so an invalid call touches
  *     neither the device nor the stream. No C++ exception crosses the ABI.
  *   - Sizes are int64_t; every dimension must be >= 0 and < 2^31, and every
- *     tensor must hold fewer than 2^40 elements. A call with a zero-sized
- *     output is a valid no-op.
+ *     tensor must hold fewer than 2^40 elements. The contraction length of a
+ *     GEMM must be below 2^24 (the kernels address a tile's rows with 32-bit
+ *     offsets). A call with a zero-sized output is a valid no-op.
  *   - Thread-safe and reentrant (no mutable global state).
  */
 #ifndef FP8BSQ_H
@@ -114,7 +115,7 @@ int transpose_quantize_128x1(const void* x, int64_t M, int64_t C,
  *   wq in : E4M3 [N, K], ws in: fp32 [N/128, K/128]   (from quantize_weight_128x128)
  *   y  out: bf16 [M, N]
  *   y[m, n] = bf16( sum_kb xs[m,kb] * ws[n/128,kb] * sum_{k in kb} xq[m,k]*wq[n,k] )
- * Shape: N % 128 == 0, K % 128 == 0, M >= 0 (any).
+ * Shape: N % 128 == 0, K % 128 == 0, M >= 0 (any), K < 2^24.
  */
 int fp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                  void* y, int64_t M, int64_t N, int64_t K, void* stream);
@@ -129,7 +130,7 @@ int fp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const fl
  *   ws   in : fp32 [N/128, K/128]                      (the same forward block scales)
  *   dx   out: bf16 [M, K]
  *   dx[m, k] = bf16( sum_nb dys[m,nb] * ws[nb,k/128] * sum_{n in nb} dyq[m,n]*wq_t[k,n] )
- * Shape: N % 128 == 0, K % 128 == 0, M >= 0 (any).
+ * Shape: N % 128 == 0, K % 128 == 0, M >= 0 (any), N < 2^24.
  */
 int fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
                    void* dx, int64_t M, int64_t N, int64_t K, void* stream);
@@ -143,7 +144,7 @@ int fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, co
  *   xq_t  in : E4M3 [K, M], xs_t  in: fp32 [K, M/128]  (transpose_quantize_128x1 of X)
  *   dw    out: bf16 [N, K]
  *   dw[n, k] = bf16( sum_mb dys_t[n,mb] * xs_t[k,mb] * sum_{m in mb} dyq_t[n,m]*xq_t[k,m] )
- * Shape: M % 128 == 0, N % 128 == 0, K % 128 == 0.
+ * Shape: M % 128 == 0, N % 128 == 0, K % 128 == 0, M < 2^24.
  */
 int fp8_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t, const float* xs_t,
                    void* dw, int64_t M, int64_t N, int64_t K, void* stream);

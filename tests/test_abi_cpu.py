@@ -90,6 +90,14 @@ def test_gemm_validation(lib):
     f = lib.fp8_gemm_fwd
     assert f(None, None, None, None, None, 0, 128, 128, None) == 0    # M == 0: no-op
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 128, 0, None) == 2      # empty contraction
+    # contraction length below 2^24 (checked before the pointers)
+    big = 1 << 24
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 1, 128, big - 128, None) == 1
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 1, 128, big, None) == 2
+    assert lib.fp8_gemm_dgrad(None, FAKE, FAKE, FAKE, FAKE, 1, big - 128, 128, None) == 1
+    assert lib.fp8_gemm_dgrad(None, FAKE, FAKE, FAKE, FAKE, 1, big, 128, None) == 2
+    assert lib.fp8_gemm_wgrad(None, FAKE, FAKE, FAKE, FAKE, big - 128, 128, 128, None) == 1
+    assert lib.fp8_gemm_wgrad(None, FAKE, FAKE, FAKE, FAKE, big, 128, 128, None) == 2
 
 
 def test_binding_has_no_cpu_fallback():
