@@ -14,6 +14,12 @@
 
 namespace fp8bsq {
 
+// Grid limits the launchers respect: at most kMaxGridY workgroups along y
+// and at most kMaxBlocks1D along x of a 1-D grid; larger problems go out as
+// several launches, each with its block offset.
+constexpr int64_t kMaxGridY = 65535;
+constexpr int64_t kMaxBlocks1D = (int64_t)1 << 22;
+
 // ============================================================================
 // 1x128: a [M, K] tensor with K % 128 == 0 is a flat array of G = M*K/128
 // groups of 128 contiguous elements, and group g's scale is xs[g]. Each group
@@ -33,14 +39,16 @@ __device__ __forceinline__ void unpack8(const u32x4& r, float* v) {
 }
 
 __global__ __launch_bounds__(ACT_THREADS) void quant_act_1x128_kernel(
-    const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, float* __restrict__ xs, int64_t G) {
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, float* __restrict__ xs, int64_t G,
+    int64_t blk0) {
   const int t = threadIdx.x;
   const int j = t & 7;
+  const int64_t blk = blk0 + blockIdx.x;
   u32x4 raw[ACT_PASSES][2];
   int64_t grp[ACT_PASSES];
 #pragma unroll
   for (int p = 0; p < ACT_PASSES; ++p) {
-    const int64_t g = (int64_t)blockIdx.x * ACT_GROUPS_PER_BLOCK + p * ACT_GROUPS_PER_PASS + (t >> 3);
+    const int64_t g = blk * ACT_GROUPS_PER_BLOCK + p * ACT_GROUPS_PER_PASS + (t >> 3);
     grp[p] = g;
     const int64_t gc = g < G ? g : G - 1;  // tail lanes re-read the last group; they store nothing
     const u32x4* src = reinterpret_cast<const u32x4*>(x + gc * 128);
@@ -82,9 +90,11 @@ __global__ __launch_bounds__(ACT_THREADS) void quant_act_1x128_kernel(
 // 8*(t/16) .. +7 and columns 8*(t%16) .. +7 of the block (eight 16-byte row
 // loads). The block amax is reduced across the wavefront with DPP and
 // shuffles, then across the four wavefronts through LDS. The optional
-// transposed copy is produced by an 8x8 byte transpose in registers.
+// transposed copy is produced by an 8x8 byte transpose in registers and an
+// LDS tile.
 // ============================================================================
 constexpr int W_THREADS = 256;
+constexpr int W_ROW_BYTES = 128 + 8;  // padded LDS row of the transposed code tile
 
 // 4x4 byte transpose: r[i] byte j -> c[j] byte i.
 __device__ __forceinline__ void transpose4x4(const uint32_t r[4], uint32_t c[4]) {
@@ -100,10 +110,11 @@ __device__ __forceinline__ void transpose4x4(const uint32_t r[4], uint32_t c[4])
 
 __global__ __launch_bounds__(W_THREADS) void quant_weight_128x128_kernel(
     const uint16_t* __restrict__ w, uint8_t* __restrict__ wq, float* __restrict__ ws,
-    uint8_t* __restrict__ wq_t, int N, int K) {
+    uint8_t* __restrict__ wq_t, int N, int K, int nb0) {
   __shared__ float red[W_THREADS / 64];
+  __shared__ __align__(16) uint8_t tile_t[128 * W_ROW_BYTES];
   const int t = threadIdx.x;
-  const int kb = blockIdx.x, nb = blockIdx.y;
+  const int kb = blockIdx.x, nb = nb0 + (int)blockIdx.y;
   const int r0 = 8 * (t >> 4), c0 = 8 * (t & 15);
   const int64_t row0 = (int64_t)nb * 128 + r0;
   const int64_t col0 = (int64_t)kb * 128 + c0;
@@ -150,6 +161,8 @@ __global__ __launch_bounds__(W_THREADS) void quant_weight_128x128_kernel(
 
   if (wq_t != nullptr) {
     // Transpose the 8x8 byte tile: out[j] holds column c0+j, rows r0..r0+7.
+    // The pieces meet in an LDS tile [column][row] and leave as 128-byte rows
+    // of wq_t (eight lanes per row), so every store fills whole cache lines.
     uint32_t out[8][2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {      // column bytes 0-3 / 4-7
@@ -165,65 +178,73 @@ __global__ __launch_bounds__(W_THREADS) void quant_weight_128x128_kernel(
     }
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj)
-      __builtin_nontemporal_store(u32x2{out[jj][0], out[jj][1]},
-                                  reinterpret_cast<u32x2*>(wq_t + (col0 + jj) * N + row0));
+      *reinterpret_cast<u32x2*>(tile_t + (c0 + jj) * W_ROW_BYTES + r0) = u32x2{out[jj][0], out[jj][1]};
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int row = (t >> 3) + 32 * h;   // column kb*128 + row of w
+      const int seg = t & 7;
+      const uint8_t* src = tile_t + row * W_ROW_BYTES + 16 * seg;
+      const u32x2 a = *reinterpret_cast<const u32x2*>(src);
+      const u32x2 b = *reinterpret_cast<const u32x2*>(src + 8);
+      __builtin_nontemporal_store(u32x4{a[0], a[1], b[0], b[1]},
+                                  reinterpret_cast<u32x4*>(wq_t + ((int64_t)kb * 128 + row) * N +
+                                                           (int64_t)nb * 128 + 16 * seg));
+    }
   }
 }
 
 // ============================================================================
-// 128x1 transposed: tile = 128 tokens x 64 channels per workgroup. Thread t
-// reads channels 8*(t%8) .. +7 of tokens 4*(t/8) .. +3 (16-byte loads, 128
-// contiguous bytes per token row). Channel amax: in-thread over 4 tokens,
-// across the 8 lanes of a wavefront that share the channels, then across the
-// 4 wavefronts through LDS. One wavefront computes the 64 channel scales; the
-// codes go to an LDS tile [64 channels][128 tokens] and leave as 128-byte rows
-// of xq_t.
+// 128x1 transposed: tile = 128 tokens x 128 channels per workgroup (one scale
+// group along the tokens). Thread t reads channels 8*(t%16) .. +7 of tokens
+// 8*(t/16) .. +7 (eight 16-byte loads; each load instruction of a wavefront
+// covers four whole 256-byte token rows). Channel amax: in-thread over 8
+// tokens, across the 4 lanes of a wavefront that share the channels, then
+// across the 4 wavefronts through LDS. The codes go to an LDS tile
+// [128 channels][128 tokens] as 8-byte pieces and leave as 128-byte rows of
+// xq_t.
 // ============================================================================
 constexpr int T_THREADS = 256;
-constexpr int T_CH = 64;
-constexpr int T_ROW_BYTES = 128 + 4;  // padded LDS row of the transposed code tile
+constexpr int T_CH = 128;
+constexpr int T_ROW_BYTES = 128 + 8;  // padded LDS row of the transposed code tile
 
 __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ xq_t, float* __restrict__ xs_t,
-    int M, int C) {
+    int M, int C, int cb0) {
   __shared__ float red[4][T_CH];
   __shared__ float p_sc[T_CH], p_r[T_CH], p_mul[T_CH];
   __shared__ __align__(16) uint8_t tile[T_CH * T_ROW_BYTES];
 
   const int t = threadIdx.x;
-  const int cb = blockIdx.x, mb = blockIdx.y;
-  const int cc = t & 7;           // channel chunk: channels 8cc .. 8cc+7 of the tile
-  const int tr = 4 * (t >> 3);    // first token of this thread's four
-  const int64_t c0 = (int64_t)cb * T_CH;
+  const int cc = t & 15;          // channel chunk: channels 8cc .. 8cc+7 of the tile
+  const int tr = 8 * (t >> 4);    // first token of this thread's eight
+  const int wave = t >> 6, lane = t & 63;
+  const int mb = blockIdx.x;
   const int64_t m0 = (int64_t)mb * 128;
+  const int64_t c0 = ((int64_t)cb0 + blockIdx.y) * T_CH;
 
-  u32x4 raw[4];
+  u32x4 raw[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
     raw[i] = __builtin_nontemporal_load(
         reinterpret_cast<const u32x4*>(x + (m0 + tr + i) * C + c0 + 8 * cc));
 
-  float v[4][8];
+  float v[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) unpack8(raw[i], v[i]);
-  float cm[8];
+  for (int i = 0; i < 8; ++i) unpack8(raw[i], v[i]);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    float mm = fmaxf(fmaxf(fabsf(v[0][e]), fabsf(v[1][e])), fmaxf(fabsf(v[2][e]), fabsf(v[3][e])));
-    // lanes with equal (lane % 8) share channels: reduce over lane bits 3..5
-    mm = fmaxf(mm, dpp_f<0x128>(mm));               // row_ror:8  (lane ^ 8 within a row of 16)
+    float mm = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mm = fmaxf(mm, fabsf(v[i][e]));
+    // lanes with equal (lane % 16) share channels: reduce over lane bits 4..5
     mm = fmaxf(mm, __shfl_xor(mm, 16, 64));
     mm = fmaxf(mm, __shfl_xor(mm, 32, 64));
-    cm[e] = mm;
-  }
-  const int wave = t >> 6, lane = t & 63;
-  if (lane < 8) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red[wave][8 * lane + e] = cm[e];
+    if (lane < 16) red[wave][8 * lane + e] = mm;
   }
   __syncthreads();
-  if (wave == 0) {
-    const int c = lane;
+  if (t < T_CH) {
+    const int c = t;
     const float m = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
     const float s = group_scale(m);
     const GroupDiv d = group_div(m, s);
@@ -238,24 +259,24 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
   for (int e = 0; e < 8; ++e) {
     const int c = 8 * cc + e;
     const float sc = p_sc[c], r = p_r[c], mul = p_mul[c];
-    float q[4];
+    float q[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = quotient(v[i][e] * mul, sc, r);
-    *reinterpret_cast<uint32_t*>(tile + c * T_ROW_BYTES + tr) = e4m3x4(q[0], q[1], q[2], q[3]);
+    for (int i = 0; i < 8; ++i) q[i] = quotient(v[i][e] * mul, sc, r);
+    *reinterpret_cast<u32x2*>(tile + c * T_ROW_BYTES + tr) =
+        u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
   }
   __syncthreads();
 
-  // 64 rows x 128 bytes = 512 16-byte pieces, two per thread, 8 lanes per row.
+  // 128 rows x 128 bytes = 1024 16-byte pieces, four per thread, 8 lanes per row.
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < 4; ++h) {
     const int row = (t >> 3) + 32 * h;
     const int seg = t & 7;
     const uint8_t* src = tile + row * T_ROW_BYTES + 16 * seg;
-    const u32x4 val = u32x4{*reinterpret_cast<const uint32_t*>(src),
-                            *reinterpret_cast<const uint32_t*>(src + 4),
-                            *reinterpret_cast<const uint32_t*>(src + 8),
-                            *reinterpret_cast<const uint32_t*>(src + 12)};
-    __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(xq_t + (c0 + row) * M + m0 + 16 * seg));
+    const u32x2 a = *reinterpret_cast<const u32x2*>(src);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(src + 8);
+    __builtin_nontemporal_store(u32x4{a[0], a[1], b[0], b[1]},
+                                reinterpret_cast<u32x4*>(xq_t + (c0 + row) * M + m0 + 16 * seg));
   }
 }
 
@@ -263,8 +284,9 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
 // Plain encoder: 4 fp32 values -> 4 E4M3 bytes per thread.
 // ============================================================================
 __global__ __launch_bounds__(256) void cast_f32_e4m3_kernel(const f32x4* __restrict__ in,
-                                                          uint32_t* __restrict__ out, int64_t n4) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+                                                          uint32_t* __restrict__ out, int64_t n4,
+                                                          int64_t blk0) {
+  const int64_t i = (blk0 + blockIdx.x) * 256 + threadIdx.x;
   if (i < n4) {
     const f32x4 v = in[i];
     out[i] = e4m3x4(v[0], v[1], v[2], v[3]);
@@ -278,32 +300,48 @@ hipError_t launch_quant_act_1x128(const void* x, int64_t M, int64_t K, uint8_t* 
                                   hipStream_t stream) {
   const int64_t G = M * (K / 128);
   const int64_t blocks = (G + ACT_GROUPS_PER_BLOCK - 1) / ACT_GROUPS_PER_BLOCK;
-  hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)blocks), dim3(ACT_THREADS), 0, stream,
-                     static_cast<const uint16_t*>(x), xq, xs, G);
+  for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocks1D) {
+    const int64_t nb = blocks - b0 < kMaxBlocks1D ? blocks - b0 : kMaxBlocks1D;
+    hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)nb), dim3(ACT_THREADS), 0, stream,
+                       static_cast<const uint16_t*>(x), xq, xs, G, b0);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_quant_weight_128x128(const void* w, int64_t N, int64_t K, uint8_t* wq, float* ws,
                                        uint8_t* wq_t, hipStream_t stream) {
-  hipLaunchKernelGGL(quant_weight_128x128_kernel, dim3((unsigned)(K / 128), (unsigned)(N / 128)),
-                     dim3(W_THREADS), 0, stream, static_cast<const uint16_t*>(w), wq, ws, wq_t,
-                     (int)N, (int)K);
+  const int64_t nbt = N / 128;
+  for (int64_t y0 = 0; y0 < nbt; y0 += kMaxGridY) {
+    const int64_t ny = nbt - y0 < kMaxGridY ? nbt - y0 : kMaxGridY;
+    hipLaunchKernelGGL(quant_weight_128x128_kernel, dim3((unsigned)(K / 128), (unsigned)ny),
+                       dim3(W_THREADS), 0, stream, static_cast<const uint16_t*>(w), wq, ws, wq_t,
+                       (int)N, (int)K, (int)y0);
+  }
   return hipGetLastError();
 }
 
+// Grid: token blocks along x (adjacent workgroups write adjacent 128-byte
+// pieces of the same xq_t rows), channel blocks along y.
 hipError_t launch_transpose_quant_128x1(const void* x, int64_t M, int64_t C, uint8_t* xq_t,
                                         float* xs_t, hipStream_t stream) {
-  hipLaunchKernelGGL(transpose_quant_128x1_kernel, dim3((unsigned)(C / T_CH), (unsigned)(M / 128)),
-                     dim3(T_THREADS), 0, stream, static_cast<const uint16_t*>(x), xq_t, xs_t,
-                     (int)M, (int)C);
+  const int64_t nc = C / T_CH;
+  for (int64_t y0 = 0; y0 < nc; y0 += kMaxGridY) {
+    const int64_t ny = nc - y0 < kMaxGridY ? nc - y0 : kMaxGridY;
+    hipLaunchKernelGGL(transpose_quant_128x1_kernel, dim3((unsigned)(M / 128), (unsigned)ny),
+                       dim3(T_THREADS), 0, stream, static_cast<const uint16_t*>(x), xq_t, xs_t,
+                       (int)M, (int)C, (int)y0);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_cast_f32_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
   const int64_t n4 = n / 4;
   const int64_t blocks = (n4 + 255) / 256;
-  hipLaunchKernelGGL(cast_f32_e4m3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     reinterpret_cast<const f32x4*>(in), reinterpret_cast<uint32_t*>(out), n4);
+  for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocks1D) {
+    const int64_t nb = blocks - b0 < kMaxBlocks1D ? blocks - b0 : kMaxBlocks1D;
+    hipLaunchKernelGGL(cast_f32_e4m3_kernel, dim3((unsigned)nb), dim3(256), 0, stream,
+                       reinterpret_cast<const f32x4*>(in), reinterpret_cast<uint32_t*>(out), n4, b0);
+  }
   return hipGetLastError();
 }
 
