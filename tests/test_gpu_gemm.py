@@ -122,6 +122,76 @@ def test_exact_wgrad(grid):
     _check_exact_or_close(host_bits(dw), ref, grid, "wgrad", 448.0 ** 2 * (os1.astype(np.float64) @ os2.astype(np.float64).T))
 
 
+# Shapes that route to the large (256 x 256) tile configuration: at least 256
+# large tiles and a ragged dimension (33 x 128 rows: the last tile is shifted
+# back and overlaps its neighbour). The ones above run the small configuration.
+
+# Block exponents vary only along the non-contracted dimension, so that every
+# K block of one output carries the same power-of-two scale product and the
+# fp32 sums stay exact (as in the tests above).
+
+def _exps_by_row(rng, rb, cb, lo, hi):
+    return np.repeat(rng.integers(lo, hi, size=(rb, 1)), cb, axis=1)
+
+
+def _exps_by_col(rng, rb, cb, lo, hi):
+    return np.repeat(rng.integers(lo, hi, size=(1, cb)), rb, axis=0)
+
+
+@pytest.mark.parametrize("grid", list(GRIDS))
+def test_exact_large_tiles_fwd(grid):
+    M, N, K = 4224, 4096, 256
+    note(f"exact fwd, large tiles ({grid}) M={M} N={N} K={K}")
+    g1, g2, g3 = inputs.tensor_streams(111, 3)
+    x = inputs.exact_operand(g1, M, K, _exps_by_row(g3, M // 128, K // 128, -3, 2), GRIDS[grid])
+    w = inputs.exact_operand(g2, N, K, _exps_by_row(g3, N // 128, K // 128, -8, -4), GRIDS[grid])
+    xq, xs = fq.quantize_act_1x128(dev_bf16(x))
+    wq, ws, _ = fq.quantize_weight_128x128(dev_bf16(w), transposed=False)
+    y = fq.fp8_gemm_fwd(xq, xs, wq, ws)
+    torch.cuda.synchronize()
+    oxq, oxs = quant.quantize_act_1x128(x)
+    owq, ows, _ = quant.quantize_weight_128x128(w)
+    ref = gemm.gemm_fwd(oxq, oxs, owq, ows)
+    _check_exact_or_close(host_bits(y), ref, grid, "fwd large tiles",
+                          448.0 ** 2 * (oxs.astype(np.float64) @ ows.astype(np.float64).repeat(128, axis=0).T))
+
+
+@pytest.mark.parametrize("grid", list(GRIDS))
+def test_exact_large_tiles_dgrad(grid):
+    M, N, K = 4224, 256, 4096
+    note(f"exact dgrad, large tiles ({grid}) M={M} N={N} K={K}")
+    g1, g2, g3 = inputs.tensor_streams(112, 3)
+    dy = inputs.exact_operand(g1, M, N, _exps_by_row(g3, M // 128, N // 128, -3, 2), GRIDS[grid])
+    w = inputs.exact_operand(g2, N, K, _exps_by_col(g3, N // 128, K // 128, -8, -4), GRIDS[grid])
+    dyq, dys = fq.quantize_act_1x128(dev_bf16(dy))
+    wq, ws, wq_t = fq.quantize_weight_128x128(dev_bf16(w))
+    dx = fq.fp8_gemm_dgrad(dyq, dys, wq_t, ws)
+    torch.cuda.synchronize()
+    odq, ods = quant.quantize_act_1x128(dy)
+    owq, ows, _ = quant.quantize_weight_128x128(w)
+    ref = gemm.gemm_dgrad(odq, ods, owq, ows)
+    _check_exact_or_close(host_bits(dx), ref, grid, "dgrad large tiles",
+                          448.0 ** 2 * (ods.astype(np.float64) @ ows.astype(np.float64).repeat(128, axis=1)))
+
+
+@pytest.mark.parametrize("grid", list(GRIDS))
+def test_exact_large_tiles_wgrad(grid):
+    M, N, K = 256, 4096, 4224
+    note(f"exact wgrad, large tiles ({grid}) M={M} N={N} K={K}")
+    g1, g2, g3 = inputs.tensor_streams(113, 3)
+    dy = inputs.exact_operand(g1, M, N, _exps_by_col(g3, M // 128, N // 128, -4, 0), GRIDS[grid])
+    x = inputs.exact_operand(g2, M, K, _exps_by_col(g3, M // 128, K // 128, -1, 3), GRIDS[grid])
+    dyq_t, dys_t = fq.transpose_quantize_128x1(dev_bf16(dy))
+    xq_t, xs_t = fq.transpose_quantize_128x1(dev_bf16(x))
+    dw = fq.fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t)
+    torch.cuda.synchronize()
+    oq1, os1 = quant.transpose_quantize_128x1(dy)
+    oq2, os2 = quant.transpose_quantize_128x1(x)
+    ref = gemm.gemm_wgrad(oq1, os1, oq2, os2)
+    _check_exact_or_close(host_bits(dw), ref, grid, "wgrad large tiles",
+                          448.0 ** 2 * (os1.astype(np.float64) @ os2.astype(np.float64).T))
+
+
 # ------------------------------------------- oracle operands, small shapes --
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (17, 384, 256), (300, 640, 1152), (64, 256, 4096)])
