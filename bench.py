@@ -2,11 +2,12 @@
 
 One step = the whole hot path for every linear of the workload:
     quantize_weight_128x128(W)            (with the transposed copy for DGrad)
-    quantize_act_1x128(X)      -> fp8_gemm_fwd      Y  = Xq Wq^T
-    quantize_act_1x128(dY)     -> fp8_gemm_dgrad    dX = dYq Wq
-    transpose_quantize_128x1(X), transpose_quantize_128x1(dY)
-                               -> fp8_gemm_wgrad    dW = dYq^T Xq
-on synthetic inputs already resident in HBM. Default workload: the four
+    quantize_dual_1x128_128x1(X)  -> fp8_gemm_fwd      Y  = Xq Wq^T   (+ Xq_t saved for WGrad)
+    quantize_dual_1x128_128x1(dY) -> fp8_gemm_dgrad    dX = dYq Wq
+                                  -> fp8_gemm_wgrad    dW = dYq^T Xq
+on synthetic inputs already resident in HBM. The dual quantizer emits the
+1x128 and the transposed 128x1 groupings from one read; --separate-quant runs
+quantize_act_1x128 and transpose_quantize_128x1 as separate launches instead. Default workload: the four
 linears of a Qwen2.5-32B-shaped layer (qkv 5120->7168, o 5120->5120,
 up 5120->27648, down 27648->5120) at 32768 tokens.
 
@@ -43,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-quant", action="store_true",
+                    help="quantize X and dY with the single-output kernels (two reads each)")
     ap.add_argument("--traffic-from", default=None,
                     help="JSON with measured HBM bytes per launch of the dominant kernel")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -59,6 +62,10 @@ def act_bytes(rows, cols):
     return rows * cols * 3 + rows * (cols // 128) * 4
 
 
+def dual_bytes(rows, cols):
+    return rows * cols * 4 + rows * (cols // 128) * 4 + cols * (rows // 128) * 4
+
+
 def weight_bytes(n, k, transposed):
     return n * k * (4 if transposed else 3) + (n // 128) * (k // 128) * 4
 
@@ -66,7 +73,7 @@ def weight_bytes(n, k, transposed):
 class Linear:
     """Device buffers and the launch list of one linear layer."""
 
-    def __init__(self, lin, passes, seed, fq, inputs, torch):
+    def __init__(self, lin, passes, seed, fq, inputs, torch, dual=True):
         self.name, self.M, self.N, self.K = lin["name"], lin["M"], lin["N"], lin["K"]
         M, N, K = self.M, self.N, self.K
         dev = "cuda"
@@ -76,12 +83,15 @@ class Linear:
         u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
         self.passes = passes
         dgrad, wgrad = "dgrad" in passes, "wgrad" in passes
+        self.dual = dual
         self.wq, self.ws = e((N, K), u8), e((N // 128, K // 128), f32)
         self.wq_t = e((K, N), u8) if dgrad else None
-        self.xq, self.xs = e((M, K), u8), e((M, K // 128), f32)
-        self.y = e((M, N), bf)
+        if "fwd" in passes:
+            self.xq, self.xs = e((M, K), u8), e((M, K // 128), f32)
+            self.y = e((M, N), bf)
         if dgrad:
             self.dyq, self.dys = e((M, N), u8), e((M, N // 128), f32)
+        if dgrad:
             self.dx = e((M, K), bf)
         if wgrad:
             self.xq_t, self.xs_t = e((K, M), u8), e((K, M // 128), f32)
@@ -90,25 +100,43 @@ class Linear:
         self.fq = fq
 
     def launches(self):
-        """(kind, key, flops, bytes, callable) for every launch of one step, in order."""
+        """(kind, key, flops, bytes, callable) for every launch of one step, in order.
+
+        X feeds the forward (1x128) and WGrad (128x1); dY feeds DGrad (1x128)
+        and WGrad (128x1). Where a tensor needs both groupings the dual
+        quantizer makes them in one launch (unless --separate-quant).
+        """
         fq, M, N, K = self.fq, self.M, self.N, self.K
+        fwd, dgrad, wgrad = ("fwd" in self.passes), ("dgrad" in self.passes), ("wgrad" in self.passes)
+        x_dual, dy_dual = self.dual and fwd and wgrad, self.dual and dgrad and wgrad
         L = []
         L.append(("quant_weight", f"{self.name}.w[{N},{K}]", 0, weight_bytes(N, K, self.wq_t is not None),
                   lambda: fq.quantize_weight_128x128(self.w, self.wq_t is not None, self.wq, self.ws, self.wq_t)))
-        L.append(("quant_act", f"{self.name}.x[{M},{K}]", 0, act_bytes(M, K),
-                  lambda: fq.quantize_act_1x128(self.x, self.xq, self.xs)))
-        L.append(("gemm_fwd", f"{self.name}.fwd[{M}x{N}x{K}]", 2 * M * N * K, M * K + N * K + 2 * M * N,
-                  lambda: fq.fp8_gemm_fwd(self.xq, self.xs, self.wq, self.ws, out=self.y)))
-        if "dgrad" in self.passes:
+        if x_dual:
+            L.append(("quant_dual", f"{self.name}.x_dual[{M},{K}]", 0, dual_bytes(M, K),
+                      lambda: fq.quantize_dual_1x128_128x1(self.x, self.xq, self.xs, self.xq_t, self.xs_t)))
+        elif fwd:
+            L.append(("quant_act", f"{self.name}.x[{M},{K}]", 0, act_bytes(M, K),
+                      lambda: fq.quantize_act_1x128(self.x, self.xq, self.xs)))
+        if fwd:
+            L.append(("gemm_fwd", f"{self.name}.fwd[{M}x{N}x{K}]", 2 * M * N * K, M * K + N * K + 2 * M * N,
+                      lambda: fq.fp8_gemm_fwd(self.xq, self.xs, self.wq, self.ws, out=self.y)))
+        if dy_dual:
+            L.append(("quant_dual", f"{self.name}.dy_dual[{M},{N}]", 0, dual_bytes(M, N),
+                      lambda: fq.quantize_dual_1x128_128x1(self.dy, self.dyq, self.dys, self.dyq_t, self.dys_t)))
+        elif dgrad:
             L.append(("quant_act", f"{self.name}.dy[{M},{N}]", 0, act_bytes(M, N),
                       lambda: fq.quantize_act_1x128(self.dy, self.dyq, self.dys)))
+        if dgrad:
             L.append(("gemm_dgrad", f"{self.name}.dgrad[{M}x{K}x{N}]", 2 * M * N * K, M * N + N * K + 2 * M * K,
                       lambda: fq.fp8_gemm_dgrad(self.dyq, self.dys, self.wq_t, self.ws, out=self.dx)))
-        if "wgrad" in self.passes:
-            L.append(("quant_transpose", f"{self.name}.x_t[{M},{K}]", 0, act_bytes(M, K),
-                      lambda: fq.transpose_quantize_128x1(self.x, self.xq_t, self.xs_t)))
-            L.append(("quant_transpose", f"{self.name}.dy_t[{M},{N}]", 0, act_bytes(M, N),
-                      lambda: fq.transpose_quantize_128x1(self.dy, self.dyq_t, self.dys_t)))
+        if wgrad:
+            if not x_dual:
+                L.append(("quant_transpose", f"{self.name}.x_t[{M},{K}]", 0, act_bytes(M, K),
+                          lambda: fq.transpose_quantize_128x1(self.x, self.xq_t, self.xs_t)))
+            if not dy_dual:
+                L.append(("quant_transpose", f"{self.name}.dy_t[{M},{N}]", 0, act_bytes(M, N),
+                          lambda: fq.transpose_quantize_128x1(self.dy, self.dyq_t, self.dys_t)))
             L.append(("gemm_wgrad", f"{self.name}.wgrad[{N}x{K}x{M}]", 2 * M * N * K, M * N + M * K + 2 * N * K,
                       lambda: fq.fp8_gemm_wgrad(self.dyq_t, self.dys_t, self.xq_t, self.xs_t, out=self.dw)))
         return L
@@ -223,7 +251,8 @@ def main():
     wl = inputs.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     print(f"[bench] workload {args.workload}: generating inputs", file=sys.stderr, flush=True)
-    layers = [Linear(lin, wl["passes"], 1000 + 17 * i, fq, inputs, torch) for i, lin in enumerate(wl["linears"])]
+    layers = [Linear(lin, wl["passes"], 1000 + 17 * i, fq, inputs, torch, dual=not args.separate_quant)
+              for i, lin in enumerate(wl["linears"])]
     launches = [l for layer in layers for l in layer.launches()]
     torch.cuda.synchronize()
     if args.calibrate_copy:
@@ -309,6 +338,7 @@ def main():
         "gemm_only_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
         "gemm_ms_per_step": round(gemm_ms, 3),
         "quant_ms_per_step": round(quant_ms, 3),
+        "quantizers": "separate" if args.separate_quant else "dual",
         "roofline": roof,
         "kernels": kernels,
     }

@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
     quantize_weight_128x128(w, transposed=True)
                                       -> (wq [N,K], ws [N/128,K/128], wq_t [K,N] or None)
     transpose_quantize_128x1(x)       -> (xq_t [C,M], xs_t [C,M/128])
+    quantize_dual_1x128_128x1(x)      -> (xq, xs, xq_t, xs_t): both of the above, one read of x
     fp8_gemm_fwd(xq, xs, wq, ws)      -> y  [M,N] bf16      (Y = X W^T)
     fp8_gemm_dgrad(dyq, dys, wq_t, ws) -> dx [M,K] bf16     (dX = dY W)
     fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t) -> dw [N,K] bf16 (dW = dY^T X)
@@ -62,6 +63,7 @@ def load_library():
         "quantize_act_1x128": ([vp, i64, i64, vp, vp, vp], i32),
         "quantize_weight_128x128": ([vp, i64, i64, vp, vp, vp, vp], i32),
         "transpose_quantize_128x1": ([vp, i64, i64, vp, vp, vp], i32),
+        "quantize_dual_1x128_128x1": ([vp, i64, i64, vp, vp, vp, vp, vp], i32),
         "fp8_gemm_fwd": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
         "fp8_gemm_dgrad": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
         "fp8_gemm_wgrad": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
@@ -150,6 +152,19 @@ def transpose_quantize_128x1(x, xq_t=None, xs_t=None):
     _check("transpose_quantize_128x1", load_library().transpose_quantize_128x1(
         _ptr(x), M, C, _ptr(xq_t), _ptr(xs_t), _stream(x)))
     return xq_t, xs_t
+
+
+def quantize_dual_1x128_128x1(x, xq=None, xs=None, xq_t=None, xs_t=None):
+    import torch
+    M, K = x.shape
+    _need(x, "x", torch.bfloat16, (M, K))
+    xq = _out(xq, "xq", torch.uint8, (M, K), x)
+    xs = _out(xs, "xs", torch.float32, (M, K // 128), x)
+    xq_t = _out(xq_t, "xq_t", torch.uint8, (K, M), x)
+    xs_t = _out(xs_t, "xs_t", torch.float32, (K, M // 128), x)
+    _check("quantize_dual_1x128_128x1", load_library().quantize_dual_1x128_128x1(
+        _ptr(x), M, K, _ptr(xq), _ptr(xs), _ptr(xq_t), _ptr(xs_t), _stream(x)))
+    return xq, xs, xq_t, xs_t
 
 
 def fp8_gemm_fwd(xq, xs, wq, ws, out=None):

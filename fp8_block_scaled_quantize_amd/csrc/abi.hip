@@ -69,6 +69,16 @@ int transpose_quantize_128x1(const void* x, int64_t M, int64_t C, uint8_t* xq_t,
   return hip_status(fp8bsq::launch_transpose_quant_128x1(x, M, C, xq_t, xs_t, as_stream(stream)));
 }
 
+int quantize_dual_1x128_128x1(const void* x, int64_t M, int64_t K, uint8_t* xq, float* xs,
+                              uint8_t* xq_t, float* xs_t, void* stream) {
+  if (!dims_ok(M, K) || M % 128 || K % 128) return FP8BSQ_ERR_SHAPE;
+  if (M == 0 || K == 0) return FP8BSQ_OK;
+  if (!x || !xq || !xs || !xq_t || !xs_t) return FP8BSQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(xs) || !aligned16(xq_t) || !aligned16(xs_t))
+    return FP8BSQ_ERR_ALIGN;
+  return hip_status(fp8bsq::launch_quant_dual(x, M, K, xq, xs, xq_t, xs_t, as_stream(stream)));
+}
+
 int fp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
                  int64_t M, int64_t N, int64_t K, void* stream) {
   if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N) || N % 128 || K % 128 || K >= kMaxContraction)

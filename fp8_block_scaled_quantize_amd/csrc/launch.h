@@ -13,6 +13,8 @@ hipError_t launch_quant_weight_128x128(const void* w, int64_t N, int64_t K, uint
                                        uint8_t* wq_t, hipStream_t stream);
 hipError_t launch_transpose_quant_128x1(const void* x, int64_t M, int64_t C, uint8_t* xq_t,
                                         float* xs_t, hipStream_t stream);
+hipError_t launch_quant_dual(const void* x, int64_t M, int64_t C, uint8_t* xq, float* xs,
+                             uint8_t* xq_t, float* xs_t, hipStream_t stream);
 hipError_t launch_cast_f32_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
 // GEMM roles. All three run the same NT kernel family: D[i][j] = sum_k P[i,k] Q[j,k]

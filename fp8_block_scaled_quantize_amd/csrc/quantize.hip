@@ -281,6 +281,103 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
 }
 
 // ============================================================================
+// Dual output: one read of a bf16 [M, C] tile of 128 tokens x 128 channels
+// emits both the 1x128 row groups (xq, xs; as quantize_act_1x128) and the
+// 128x1 token groups written transposed (xq_t, xs_t; as
+// transpose_quantize_128x1). Thread layout and the transposed half are those
+// of the 128x1 kernel; a row group's amax is this thread's 8 channels reduced
+// over the 16 lanes that share its 8 tokens (one DPP row).
+// ============================================================================
+__global__ __launch_bounds__(T_THREADS) void quant_dual_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, float* __restrict__ xs,
+    uint8_t* __restrict__ xq_t, float* __restrict__ xs_t, int M, int C, int cb0) {
+  __shared__ float red[4][T_CH];
+  __shared__ float p_sc[T_CH], p_r[T_CH], p_mul[T_CH];
+  __shared__ __align__(16) uint8_t tile[T_CH * T_ROW_BYTES];
+
+  const int t = threadIdx.x;
+  const int cc = t & 15;          // channel chunk: channels 8cc .. 8cc+7 of the tile
+  const int tr = 8 * (t >> 4);    // first token of this thread's eight
+  const int wave = t >> 6, lane = t & 63;
+  const int mb = blockIdx.x;
+  const int cb = cb0 + (int)blockIdx.y;
+  const int64_t m0 = (int64_t)mb * 128;
+  const int64_t c0 = (int64_t)cb * T_CH;
+
+  u32x4 raw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    raw[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(x + (m0 + tr + i) * C + c0 + 8 * cc));
+
+  float v[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) unpack8(raw[i], v[i]);
+
+  // ---- 1x128 row groups: token m0+tr+i, channels c0 .. c0+127 ----
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[i][e]));
+    m = max16(m);
+    const float s = group_scale(m);
+    const GroupDiv d = group_div(m, s);
+    float q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = quotient(v[i][e] * d.xmul, d.sc, d.r);
+    const int64_t row = m0 + tr + i;
+    __builtin_nontemporal_store(u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])},
+                                reinterpret_cast<u32x2*>(xq + row * C + c0 + 8 * cc));
+    if (cc == 0) xs[row * (C / 128) + cb] = s;
+  }
+
+  // ---- 128x1 token groups, written transposed ----
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float mm = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mm = fmaxf(mm, fabsf(v[i][e]));
+    mm = fmaxf(mm, __shfl_xor(mm, 16, 64));
+    mm = fmaxf(mm, __shfl_xor(mm, 32, 64));
+    if (lane < 16) red[wave][8 * lane + e] = mm;
+  }
+  __syncthreads();
+  if (t < T_CH) {
+    const int c = t;
+    const float m = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+    const float s = group_scale(m);
+    const GroupDiv d = group_div(m, s);
+    p_sc[c] = d.sc;
+    p_r[c] = d.r;
+    p_mul[c] = d.xmul;
+    xs_t[(c0 + c) * (M / 128) + mb] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = 8 * cc + e;
+    const float sc = p_sc[c], r = p_r[c], mul = p_mul[c];
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = quotient(v[i][e] * mul, sc, r);
+    *reinterpret_cast<u32x2*>(tile + c * T_ROW_BYTES + tr) =
+        u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int row = (t >> 3) + 32 * h;
+    const int seg = t & 7;
+    const uint8_t* src = tile + row * T_ROW_BYTES + 16 * seg;
+    const u32x2 a = *reinterpret_cast<const u32x2*>(src);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(src + 8);
+    __builtin_nontemporal_store(u32x4{a[0], a[1], b[0], b[1]},
+                                reinterpret_cast<u32x4*>(xq_t + (c0 + row) * M + m0 + 16 * seg));
+  }
+}
+
+// ============================================================================
 // Plain encoder: 4 fp32 values -> 4 E4M3 bytes per thread.
 // ============================================================================
 __global__ __launch_bounds__(256) void cast_f32_e4m3_kernel(const f32x4* __restrict__ in,
@@ -330,6 +427,18 @@ hipError_t launch_transpose_quant_128x1(const void* x, int64_t M, int64_t C, uin
     hipLaunchKernelGGL(transpose_quant_128x1_kernel, dim3((unsigned)(M / 128), (unsigned)ny),
                        dim3(T_THREADS), 0, stream, static_cast<const uint16_t*>(x), xq_t, xs_t,
                        (int)M, (int)C, (int)y0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_dual(const void* x, int64_t M, int64_t C, uint8_t* xq, float* xs,
+                             uint8_t* xq_t, float* xs_t, hipStream_t stream) {
+  const int64_t nc = C / T_CH;
+  for (int64_t y0 = 0; y0 < nc; y0 += kMaxGridY) {
+    const int64_t ny = nc - y0 < kMaxGridY ? nc - y0 : kMaxGridY;
+    hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)(M / 128), (unsigned)ny), dim3(T_THREADS), 0,
+                       stream, static_cast<const uint16_t*>(x), xq, xs, xq_t, xs_t, (int)M, (int)C,
+                       (int)y0);
   }
   return hipGetLastError();
 }

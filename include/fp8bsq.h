@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define FP8BSQ_ABI_VERSION 1
+#define FP8BSQ_ABI_VERSION 2
 
 /* Status codes. */
 #define FP8BSQ_OK 0
@@ -104,6 +104,24 @@ int quantize_weight_128x128(const void* w, int64_t N, int64_t K,
  */
 int transpose_quantize_128x1(const void* x, int64_t M, int64_t C,
                              uint8_t* xq_t, float* xs_t, void* stream);
+
+/*
+ * quantize_dual_1x128_128x1 -- both groupings of one activation tensor from a
+ * single read: the 1x128 row groups of quantize_act_1x128 (the forward or
+ * DGrad operand) and the 128x1 token groups of transpose_quantize_128x1 (the
+ * WGrad operand, which the forward also keeps as the saved FP8 activation).
+ * Source: "Esquema de Cuantización": activations in 1x128 groups for the
+ * forward, 1x128 / 128x1 groupings for WGrad, activations stored in FP8
+ * between forward and backward.
+ *
+ *   x    in : bf16 [M, K]
+ *   xq   out: E4M3 [M, K],    xs   out: fp32 [M, K/128]   (as quantize_act_1x128)
+ *   xq_t out: E4M3 [K, M],    xs_t out: fp32 [K, M/128]   (as transpose_quantize_128x1)
+ * Every output is bit-identical to the corresponding single-output call.
+ * Shape: M % 128 == 0, K % 128 == 0.
+ */
+int quantize_dual_1x128_128x1(const void* x, int64_t M, int64_t K, uint8_t* xq, float* xs,
+                              uint8_t* xq_t, float* xs_t, void* stream);
 
 /*
  * fp8_gemm_fwd -- forward / rollout GEMM, Y = Xq . Wq^T.

@@ -29,7 +29,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"quantize_act_1x128", "quantize_weight_128x128", "transpose_quantize_128x1",
-                          "fp8_gemm_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
+                          "quantize_dual_1x128_128x1", "fp8_gemm_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
                           "fp8bsq_strerror", "fp8bsq_abi_version", "fp8bsq_cast_f32_e4m3"}
     for n in names:
         assert hasattr(lib, n), n
@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_strerror(lib):
     lib.fp8bsq_abi_version.restype = ctypes.c_int
-    assert lib.fp8bsq_abi_version() == 1
+    assert lib.fp8bsq_abi_version() == 2
     lib.fp8bsq_strerror.restype = ctypes.c_char_p
     lib.fp8bsq_strerror.argtypes = [ctypes.c_int]
     for code in range(5):
@@ -74,6 +74,18 @@ def test_quantizer_validation(lib):
     c.argtypes = [P, P, I64, P]
     assert c(FAKE, FAKE, 6, None) == 2
     assert c(None, FAKE, 8, None) == 1
+
+
+def test_dual_quantizer_validation(lib):
+    d = lib.quantize_dual_1x128_128x1
+    d.argtypes = [P, I64, I64, P, P, P, P, P]
+    d.restype = ctypes.c_int
+    assert d(FAKE, 64, 128, FAKE, FAKE, FAKE, FAKE, None) == 2        # tokens grouped by 128
+    assert d(FAKE, 128, 96, FAKE, FAKE, FAKE, FAKE, None) == 2        # channels grouped by 128
+    assert d(FAKE, -128, 128, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert d(FAKE, 128, 128, FAKE, FAKE, None, FAKE, None) == 1       # every output is required
+    assert d(FAKE, 128, 128, FAKE, FAKE, FAKE, MISALIGNED, None) == 3
+    assert d(None, 0, 128, None, None, None, None, None) == 0         # empty: no-op
 
 
 def test_gemm_validation(lib):

@@ -262,14 +262,29 @@ def test_gemm_determinism():
 # --------------------------------------------- full-size workloads, sampled --
 
 def _check_linear(lin, passes, seed):
-    """Run the linear's passes on the GPU at full size; check sampled outputs."""
+    """Run the linear's passes on the GPU at full size, quantizing as the
+    benchmark does (the dual quantizer wherever a tensor needs both
+    groupings); check sampled outputs."""
     M, N, K = lin["M"], lin["N"], lin["K"]
     t = inputs.linear_tensors_device(lin, seed=seed)
     x, w, dy = t["x"], t["w"], t["dy"]
-    if "fwd" in passes:
-        note(f"{lin['name']} fwd M={M} N={N} K={K}")
+    fwd, dgrad, wgrad = "fwd" in passes, "dgrad" in passes, "wgrad" in passes
+    xq = xs = xq_t = xs_t = dyq = dys = dyq_t = dys_t = None
+    if fwd and wgrad:
+        xq, xs, xq_t, xs_t = fq.quantize_dual_1x128_128x1(x)
+    elif fwd:
         xq, xs = fq.quantize_act_1x128(x)
-        wq, ws, _ = fq.quantize_weight_128x128(w, transposed=False)
+    if dgrad and wgrad:
+        dyq, dys, dyq_t, dys_t = fq.quantize_dual_1x128_128x1(dy)
+    elif dgrad:
+        dyq, dys = fq.quantize_act_1x128(dy)
+    if wgrad and xq_t is None:
+        xq_t, xs_t = fq.transpose_quantize_128x1(x)
+    if wgrad and dyq_t is None:
+        dyq_t, dys_t = fq.transpose_quantize_128x1(dy)
+    wq, ws, wq_t = fq.quantize_weight_128x128(w, transposed=dgrad)
+    if fwd:
+        note(f"{lin['name']} fwd M={M} N={N} K={K}")
         y = fq.fp8_gemm_fwd(xq, xs, wq, ws)
         torch.cuda.synchronize()
         rows = sample_indices(M, 48, seed)
@@ -278,10 +293,9 @@ def _check_linear(lin, passes, seed):
         owq, ows, _ = quant.quantize_weight_128x128(host_bits(w[bands]))
         ref = gemm.gemm_fwd(oxq, oxs, owq, ows)
         _assert_close(host_bits(y[rows][:, bands]), ref, f"{lin['name']} fwd")
-    if "dgrad" in passes:
+        del y
+    if dgrad:
         note(f"{lin['name']} dgrad M={M} N={N} K={K}")
-        dyq, dys = fq.quantize_act_1x128(dy)
-        wq, ws, wq_t = fq.quantize_weight_128x128(w)
         dx = fq.fp8_gemm_dgrad(dyq, dys, wq_t, ws)
         torch.cuda.synchronize()
         rows = sample_indices(M, 48, seed + 2)
@@ -290,10 +304,9 @@ def _check_linear(lin, passes, seed):
         owq, ows, _ = quant.quantize_weight_128x128(host_bits(w[:, kb]))
         ref = gemm.gemm_dgrad(odq, ods, owq, ows)
         _assert_close(host_bits(dx[rows][:, kb]), ref, f"{lin['name']} dgrad")
-    if "wgrad" in passes:
+        del dx
+    if wgrad:
         note(f"{lin['name']} wgrad M={M} N={N} K={K}")
-        dyq_t, dys_t = fq.transpose_quantize_128x1(dy)
-        xq_t, xs_t = fq.transpose_quantize_128x1(x)
         dw = fq.fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t)
         torch.cuda.synchronize()
         ns = sample_indices(N, 40, seed + 4)
@@ -302,7 +315,8 @@ def _check_linear(lin, passes, seed):
         oq2, os2 = quant.transpose_quantize_128x1(host_bits(x[:, ks]))
         ref = gemm.gemm_wgrad(oq1, os1, oq2, os2)
         _assert_close(host_bits(dw[ns][:, ks]), ref, f"{lin['name']} wgrad")
-    del t, x, w, dy
+        del dw
+    del t, x, w, dy, xq, xs, xq_t, xs_t, dyq, dys, dyq_t, dys_t, wq, ws, wq_t
     torch.cuda.empty_cache()
 
 

@@ -150,6 +150,62 @@ def test_transpose_full_size_sampled_and_identity():
     assert torch.equal(qt2, q1) and torch.equal(st2, s1)
 
 
+# ------------------------------------------------------------ dual output --
+
+@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (384, 640), (512, 1152)])
+def test_dual_matches_oracle(shape):
+    note(f"dual 1x128 + 128x1 {shape}")
+    x = _np_bf16(*shape, seed=5 * sum(shape))
+    xq, xs, qt, st = fq.quantize_dual_1x128_128x1(dev_bf16(x))
+    torch.cuda.synchronize()
+    oq, os_ = quant.quantize_act_1x128(x)
+    oqt, ost = quant.transpose_quantize_128x1(x)
+    assert_bytes_equal(host(xq), oq, "xq", x)
+    assert_bytes_equal(host(xs), os_, "xs")
+    assert np.array_equal(host(qt), oqt)
+    assert np.array_equal(host(st), ost)
+
+
+def test_dual_edge_groups():
+    note("dual: zero, -0, subnormal, tiny and bf16-max groups along both groupings")
+    x = _np_bf16(256, 384, seed=41)
+    x[0, :] = 0                                   # an all-zero row
+    x[1, :] = 0x8000                              # an all -0.0 row
+    x[2, :] = 0x0001                              # smallest subnormal everywhere
+    x[3, ::3] = 0x8001
+    x[4:20, :] = inputs.f32_to_bf16_bits(                 # amax far below 2^-64
+        e4m3.bf16_bits_to_f32(x[4:20, :]) * np.float32(2.0 ** -100))
+    x[:, 5] = 0x7F7F                              # largest finite bf16 in one channel
+    x[128:, 130] = 0                              # a zero 128x1 group
+    x[128:, 131] = 0x8000                         # a -0.0 128x1 group
+    xq, xs, qt, st = fq.quantize_dual_1x128_128x1(dev_bf16(x))
+    torch.cuda.synchronize()
+    oq, os_ = quant.quantize_act_1x128(x)
+    oqt, ost = quant.transpose_quantize_128x1(x)
+    assert_bytes_equal(host(xs), os_, "xs")
+    assert_bytes_equal(host(xq), oq, "xq", x)
+    assert np.array_equal(host(st), ost)
+    assert np.array_equal(host(qt), oqt)
+
+
+def test_dual_full_size_equals_single_output_kernels():
+    M, C = 32768, 27648
+    note(f"dual full size [{M},{C}] vs the single-output kernels (all bytes) and the oracle (sampled)")
+    x = inputs.bf16_normal_device((M, C), 1.0, 0.01, seed=23)
+    xq, xs, qt, st = fq.quantize_dual_1x128_128x1(x)
+    q1, s1 = fq.quantize_act_1x128(x)
+    q2, s2 = fq.transpose_quantize_128x1(x)
+    torch.cuda.synchronize()
+    assert torch.equal(xq, q1) and torch.equal(xs, s1)
+    assert torch.equal(qt, q2) and torch.equal(st, s2)
+    rows = sample_indices(M, 24, seed=3)
+    oq, os_ = quant.quantize_act_1x128(host_bits(x[rows]))
+    assert np.array_equal(host(xq[rows]), oq) and np.array_equal(host(xs[rows]), os_)
+    cols = sample_indices(C, 24, seed=4)
+    oqt, ost = quant.transpose_quantize_128x1(host_bits(x[:, cols]))
+    assert np.array_equal(host(qt[cols]), oqt) and np.array_equal(host(st[cols]), ost)
+
+
 # ------------------------------------------------------------------ codec --
 
 def test_cast_sweep_matches_oracle():
@@ -174,7 +230,9 @@ def test_determinism():
     d = fq.transpose_quantize_128x1(x)
     e = fq.quantize_weight_128x128(x)
     f = fq.quantize_weight_128x128(x)
+    g = fq.quantize_dual_1x128_128x1(x)
+    h = fq.quantize_dual_1x128_128x1(x)
     torch.cuda.synchronize()
-    for u, w in ((a, b), (c, d), (e, f)):
+    for u, w in ((a, b), (c, d), (e, f), (g, h)):
         for s, t in zip(u, w):
             assert torch.equal(s, t)
