@@ -203,7 +203,11 @@ def summarize_trace(path):
     import csv
     groups = {}
     for r in csv.DictReader(open(path)):
-        key = (_short(r["Kernel_Name"]), r.get("Grid_Size", r.get("Grid_Size_X", "")))
+        if "Grid_Size" in r:
+            grid = r["Grid_Size"]
+        else:
+            grid = str(int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y") or 1) * int(r.get("Grid_Size_Z") or 1))
+        key = (_short(r["Kernel_Name"]), grid)
         d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
         groups.setdefault(key, []).append(d)
     rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
