@@ -206,6 +206,40 @@ def test_dual_full_size_equals_single_output_kernels():
     assert np.array_equal(host(qt[cols]), oqt) and np.array_equal(host(st[cols]), ost)
 
 
+# ------------------------------------------------- grid-limit launch split --
+
+def test_launch_split_beyond_grid_y_limit():
+    # 65536 channel (or row) blocks: one more than a launch's y extent, so the
+    # launchers issue a second launch with a block offset.
+    C = 65536 * 128
+    note(f"transpose / dual / weight quantizers past the grid limit: [128, {C}] and [{C}, 128]")
+    x = inputs.bf16_normal_device((128, C), 1.0, 0.01, seed=29)
+    cols = np.unique(np.concatenate([sample_indices(C, 24, seed=5), np.arange(C - 130, C)]))
+    qt, st = fq.transpose_quantize_128x1(x)
+    torch.cuda.synchronize()
+    oqt, ost = quant.transpose_quantize_128x1(host_bits(x[:, cols]))
+    assert np.array_equal(host(qt[cols]), oqt) and np.array_equal(host(st[cols]), ost)
+    del qt, st
+    xq, xs, qt, st = fq.quantize_dual_1x128_128x1(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(qt[cols]), oqt) and np.array_equal(host(st[cols]), ost)
+    band = slice(C - 128 * 3, C)
+    oq, os_ = quant.quantize_act_1x128(host_bits(x[:, band]))
+    assert np.array_equal(host(xq[:, band]), oq)
+    assert np.array_equal(host(xs[:, (C - 384) // 128:]), os_)
+    del xq, xs, qt, st
+    w = x.t().contiguous()
+    del x
+    wq, ws, wq_t = fq.quantize_weight_128x128(w)
+    torch.cuda.synchronize()
+    for rb in (0, 31337, 65535):
+        rows = slice(128 * rb, 128 * rb + 128)
+        owq, ows, owq_t = quant.quantize_weight_128x128(host_bits(w[rows]))
+        assert np.array_equal(host(wq[rows]), owq)
+        assert np.array_equal(host(ws[rb:rb + 1]), ows)
+        assert np.array_equal(host(wq_t[:, rows]), owq_t)
+
+
 # ------------------------------------------------------------------ codec --
 
 def test_cast_sweep_matches_oracle():
