@@ -16,6 +16,9 @@ What it follows (the Jet-RL pages; see each function for the exact passage):
   groups; gradients between operators stay bf16; saved activations are FP8.
 * Same page, "Arquitectura Central": master weights are bf16, and rollout and
   training forward share one quantization flow.
+* Same page, "Esquema de Cuantización" (saved activations in FP8, fused with
+  the producing operator) and "Implementación" (quantization fused with the
+  activation and RMSNorm kernels): the RMSNorm and SwiGLU producers.
 
 Numeric choices the pages leave open (format OCP E4M3, fp32 scale amax/448,
 round-to-nearest-even, bf16 GEMM output, the parity tolerance) are the ones the
@@ -25,10 +28,12 @@ Modules:
     e4m3   -- the OCP E4M3 codec (decode table, RNE encoder), bf16 helpers
     quant  -- the three group quantizers (1x128, 128x128, 128x1 transposed)
     gemm   -- fp64 GEMMs over dequantized operands, bf16 RNE, tolerance check
+    fused  -- RMSNorm and SwiGLU (fp64, rounded once to bf16), whose outputs
+              the fused kernels quantize
 
 Every function is pinned by ``tests/test_oracle_*.py`` against something other
 than itself: brute-force searches, exact rational arithmetic, closed forms,
 invariants and an independent library (torch's float8_e4m3fn cast).
 """
 
-from . import e4m3, quant, gemm  # noqa: F401
+from . import e4m3, quant, gemm, fused  # noqa: F401
