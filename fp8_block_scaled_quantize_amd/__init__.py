@@ -14,6 +14,10 @@ Entry points (same names as the C ABI):
                                       -> (wq [N,K], ws [N/128,K/128], wq_t [K,N] or None)
     transpose_quantize_128x1(x)       -> (xq_t [C,M], xs_t [C,M/128])
     quantize_dual_1x128_128x1(x)      -> (xq, xs, xq_t, xs_t): both of the above, one read of x
+    rmsnorm_quantize_1x128(x, gamma, eps, transposed=False, write_y=False)
+                                      -> (xq, xs, xq_t, xs_t, rstd, y): RMSNorm, its output quantized
+    swiglu_quantize_1x128(gate, up, transposed=False, write_h=False)
+                                      -> (hq, hs, hq_t, hs_t, h): silu(gate)*up, quantized
     fp8_gemm_fwd(xq, xs, wq, ws)      -> y  [M,N] bf16      (Y = X W^T)
     fp8_gemm_dgrad(dyq, dys, wq_t, ws) -> dx [M,K] bf16     (dX = dY W)
     fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t) -> dw [N,K] bf16 (dW = dY^T X)
@@ -64,6 +68,8 @@ def load_library():
         "quantize_weight_128x128": ([vp, i64, i64, vp, vp, vp, vp], i32),
         "transpose_quantize_128x1": ([vp, i64, i64, vp, vp, vp], i32),
         "quantize_dual_1x128_128x1": ([vp, i64, i64, vp, vp, vp, vp, vp], i32),
+        "rmsnorm_quantize_1x128": ([vp, vp, ctypes.c_float, i64, i64, vp, vp, vp, vp, vp, vp, vp], i32),
+        "swiglu_quantize_1x128": ([vp, vp, i64, i64, vp, vp, vp, vp, vp, vp], i32),
         "fp8_gemm_fwd": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
         "fp8_gemm_dgrad": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
         "fp8_gemm_wgrad": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
@@ -165,6 +171,46 @@ def quantize_dual_1x128_128x1(x, xq=None, xs=None, xq_t=None, xs_t=None):
     _check("quantize_dual_1x128_128x1", load_library().quantize_dual_1x128_128x1(
         _ptr(x), M, K, _ptr(xq), _ptr(xs), _ptr(xq_t), _ptr(xs_t), _stream(x)))
     return xq, xs, xq_t, xs_t
+
+
+def rmsnorm_quantize_1x128(x, gamma, eps=1e-6, transposed=False, write_y=False,
+                           xq=None, xs=None, xq_t=None, xs_t=None, rstd=None, y=None):
+    import torch
+    M, K = x.shape
+    _need(x, "x", torch.bfloat16, (M, K))
+    _need(gamma, "gamma", torch.bfloat16, (K,))
+    xq = _out(xq, "xq", torch.uint8, (M, K), x)
+    xs = _out(xs, "xs", torch.float32, (M, K // 128), x)
+    rstd = _out(rstd, "rstd", torch.float32, (M,), x)
+    if transposed:
+        xq_t = _out(xq_t, "xq_t", torch.uint8, (K, M), x)
+        xs_t = _out(xs_t, "xs_t", torch.float32, (K, M // 128), x)
+    else:
+        xq_t = xs_t = None
+    y = _out(y, "y", torch.bfloat16, (M, K), x) if write_y else None
+    _check("rmsnorm_quantize_1x128", load_library().rmsnorm_quantize_1x128(
+        _ptr(x), _ptr(gamma), float(eps), M, K, _ptr(rstd), _ptr(y), _ptr(xq), _ptr(xs),
+        _ptr(xq_t), _ptr(xs_t), _stream(x)))
+    return xq, xs, xq_t, xs_t, rstd, y
+
+
+def swiglu_quantize_1x128(gate, up, transposed=False, write_h=False,
+                          hq=None, hs=None, hq_t=None, hs_t=None, h=None):
+    import torch
+    M, N = gate.shape
+    _need(gate, "gate", torch.bfloat16, (M, N))
+    _need(up, "up", torch.bfloat16, (M, N))
+    hq = _out(hq, "hq", torch.uint8, (M, N), gate)
+    hs = _out(hs, "hs", torch.float32, (M, N // 128), gate)
+    if transposed:
+        hq_t = _out(hq_t, "hq_t", torch.uint8, (N, M), gate)
+        hs_t = _out(hs_t, "hs_t", torch.float32, (N, M // 128), gate)
+    else:
+        hq_t = hs_t = None
+    h = _out(h, "h", torch.bfloat16, (M, N), gate) if write_h else None
+    _check("swiglu_quantize_1x128", load_library().swiglu_quantize_1x128(
+        _ptr(gate), _ptr(up), M, N, _ptr(h), _ptr(hq), _ptr(hs), _ptr(hq_t), _ptr(hs_t), _stream(gate)))
+    return hq, hs, hq_t, hs_t, h
 
 
 def fp8_gemm_fwd(xq, xs, wq, ws, out=None):

@@ -1,7 +1,8 @@
-// The C ABI of the library: argument validation, then one launch per call.
+// The C ABI of the library: argument validation, then the kernel launches.
 //
 // Every check runs before any HIP runtime call, so an invalid call returns its
 // status without touching the device or the stream.
+#include <math.h>
 #include "../../include/fp8bsq.h"
 
 #include <hip/hip_runtime.h>
@@ -36,6 +37,7 @@ const char* fp8bsq_strerror(int status) {
     case FP8BSQ_ERR_SHAPE: return "unsupported shape (negative, too large, or not a multiple of 128 where required)";
     case FP8BSQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case FP8BSQ_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case FP8BSQ_ERR_VALUE: return "a scalar argument is out of range";
     default: return "unknown status";
   }
 }
@@ -77,6 +79,33 @@ int quantize_dual_1x128_128x1(const void* x, int64_t M, int64_t K, uint8_t* xq, 
   if (!aligned16(x) || !aligned16(xq) || !aligned16(xs) || !aligned16(xq_t) || !aligned16(xs_t))
     return FP8BSQ_ERR_ALIGN;
   return hip_status(fp8bsq::launch_quant_dual(x, M, K, xq, xs, xq_t, xs_t, as_stream(stream)));
+}
+
+int rmsnorm_quantize_1x128(const void* x, const void* gamma, float eps, int64_t M, int64_t K,
+                           float* rstd, void* y, uint8_t* xq, float* xs, uint8_t* xq_t, float* xs_t,
+                           void* stream) {
+  const bool tr = xq_t != nullptr || xs_t != nullptr;
+  if (!dims_ok(M, K) || K % 128 || (tr && M % 128)) return FP8BSQ_ERR_SHAPE;
+  if (!(eps >= 0.0f) || eps == INFINITY) return FP8BSQ_ERR_VALUE;
+  if (M == 0 || K == 0) return FP8BSQ_OK;
+  if (!x || !gamma || !rstd || !xq || !xs || (tr && (!xq_t || !xs_t))) return FP8BSQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(xq) || !aligned16(xs) || (y && !aligned16(y)) ||
+      (tr && (!aligned16(xq_t) || !aligned16(xs_t))))
+    return FP8BSQ_ERR_ALIGN;
+  return hip_status(fp8bsq::launch_rmsnorm_quant(x, gamma, eps, M, K, rstd, y, xq, xs, xq_t, xs_t,
+                                                 as_stream(stream)));
+}
+
+int swiglu_quantize_1x128(const void* gate, const void* up, int64_t M, int64_t N, void* h,
+                          uint8_t* hq, float* hs, uint8_t* hq_t, float* hs_t, void* stream) {
+  const bool tr = hq_t != nullptr || hs_t != nullptr;
+  if (!dims_ok(M, N) || N % 128 || (tr && M % 128)) return FP8BSQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BSQ_OK;
+  if (!gate || !up || !hq || !hs || (tr && (!hq_t || !hs_t))) return FP8BSQ_ERR_NULL;
+  if (!aligned16(gate) || !aligned16(up) || !aligned16(hq) || !aligned16(hs) || (h && !aligned16(h)) ||
+      (tr && (!aligned16(hq_t) || !aligned16(hs_t))))
+    return FP8BSQ_ERR_ALIGN;
+  return hip_status(fp8bsq::launch_swiglu_quant(gate, up, M, N, h, hq, hs, hq_t, hs_t, as_stream(stream)));
 }
 
 int fp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,

@@ -15,6 +15,11 @@ hipError_t launch_transpose_quant_128x1(const void* x, int64_t M, int64_t C, uin
                                         float* xs_t, hipStream_t stream);
 hipError_t launch_quant_dual(const void* x, int64_t M, int64_t C, uint8_t* xq, float* xs,
                              uint8_t* xq_t, float* xs_t, hipStream_t stream);
+hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, float eps, int64_t M, int64_t K,
+                                float* rstd, void* y, uint8_t* xq, float* xs, uint8_t* xq_t,
+                                float* xs_t, hipStream_t stream);
+hipError_t launch_swiglu_quant(const void* gate, const void* up, int64_t M, int64_t N, void* h,
+                               uint8_t* hq, float* hs, uint8_t* hq_t, float* hs_t, hipStream_t stream);
 hipError_t launch_cast_f32_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
 // GEMM roles. All three run the same NT kernel family: D[i][j] = sum_k P[i,k] Q[j,k]

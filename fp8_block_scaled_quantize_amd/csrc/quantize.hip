@@ -281,16 +281,37 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
 }
 
 // ============================================================================
-// Dual output: one read of a bf16 [M, C] tile of 128 tokens x 128 channels
-// emits both the 1x128 row groups (xq, xs; as quantize_act_1x128) and the
-// 128x1 token groups written transposed (xq_t, xs_t; as
-// transpose_quantize_128x1). Thread layout and the transposed half are those
-// of the 128x1 kernel; a row group's amax is this thread's 8 channels reduced
-// over the 16 lanes that share its 8 tokens (one DPP row).
+// Produce-and-quantize: one read of a tile of 128 tokens x 128 channels
+// produces bf16 values and emits their 1x128 row groups (xq, xs; as
+// quantize_act_1x128) and, optionally, their 128x1 token groups written
+// transposed (xq_t, xs_t; as transpose_quantize_128x1). The producer is
+//   EW_COPY     the input itself (the dual quantizer);
+//   EW_RMSNORM  y = bf16(fl32(fl32(x * rstd[m]) * gamma[c]));
+//   EW_SWIGLU   y = bf16(fl32(silu(g) * u)), silu(g) = fl32(g / fl32(1 + expf(-g))).
+// Thread layout and the transposed half are those of the 128x1 kernel; a row
+// group's amax is this thread's 8 channels reduced over the 16 lanes that
+// share its 8 tokens (one DPP row). Without the transposed output M may be
+// ragged: rows past M are read clamped and never stored.
 // ============================================================================
-__global__ __launch_bounds__(T_THREADS) void quant_dual_kernel(
-    const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, float* __restrict__ xs,
-    uint8_t* __restrict__ xq_t, float* __restrict__ xs_t, int M, int C, int cb0) {
+enum EwOp { EW_COPY = 0, EW_RMSNORM = 1, EW_SWIGLU = 2 };
+
+struct EwArgs {
+  const uint16_t* x;      // bf16 [M, C]: input (COPY), x (RMSNORM) or gate g (SWIGLU)
+  const uint16_t* x2;     // bf16 [M, C]: up projection u (SWIGLU)
+  const uint16_t* gamma;  // bf16 [C] (RMSNORM)
+  const float* rstd;      // fp32 [M] (RMSNORM)
+  uint16_t* y;            // bf16 [M, C] copy of the produced values, or null
+  uint8_t* xq;
+  float* xs;
+  uint8_t* xq_t;          // null: no 128x1 output
+  float* xs_t;
+  int M, C, cb0;
+};
+
+__device__ __forceinline__ float round_bf16(float v) { return __uint_as_float(f32_to_bf16_rne(v) << 16); }
+
+template <int OP>
+__global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
   __shared__ float red[4][T_CH];
   __shared__ float p_sc[T_CH], p_r[T_CH], p_mul[T_CH];
   __shared__ __align__(16) uint8_t tile[T_CH * T_ROW_BYTES];
@@ -300,19 +321,59 @@ __global__ __launch_bounds__(T_THREADS) void quant_dual_kernel(
   const int tr = 8 * (t >> 4);    // first token of this thread's eight
   const int wave = t >> 6, lane = t & 63;
   const int mb = blockIdx.x;
-  const int cb = cb0 + (int)blockIdx.y;
+  const int cb = a.cb0 + (int)blockIdx.y;
   const int64_t m0 = (int64_t)mb * 128;
   const int64_t c0 = (int64_t)cb * T_CH;
+  const int C = a.C;
 
-  u32x4 raw[8];
+  u32x4 raw[8], raw2[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    raw[i] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(x + (m0 + tr + i) * C + c0 + 8 * cc));
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = min(m0 + tr + i, (int64_t)a.M - 1);
+    raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x + row * C + c0 + 8 * cc));
+    if (OP == EW_SWIGLU)
+      raw2[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x2 + row * C + c0 + 8 * cc));
+  }
 
   float v[8][8];
+  if (OP == EW_COPY) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) unpack8(raw[i], v[i]);
+    for (int i = 0; i < 8; ++i) unpack8(raw[i], v[i]);
+  } else if (OP == EW_RMSNORM) {
+    float gm[8];
+    unpack8(*reinterpret_cast<const u32x4*>(a.gamma + c0 + 8 * cc), gm);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float r = a.rstd[min(m0 + tr + i, (int64_t)a.M - 1)];
+      float xv[8];
+      unpack8(raw[i], xv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = round_bf16((xv[e] * r) * gm[e]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float gv[8], uv[8];
+      unpack8(raw[i], gv);
+      unpack8(raw2[i], uv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float sg = gv[e] / (1.0f + expf(-gv[e]));
+        v[i][e] = round_bf16(sg * uv[e]);
+      }
+    }
+  }
+  if (OP != EW_COPY && a.y != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t row = m0 + tr + i;
+      if (row < a.M)
+        __builtin_nontemporal_store(
+            u32x4{pack_bf16x2(v[i][0], v[i][1]), pack_bf16x2(v[i][2], v[i][3]),
+                  pack_bf16x2(v[i][4], v[i][5]), pack_bf16x2(v[i][6], v[i][7])},
+            reinterpret_cast<u32x4*>(a.y + row * C + c0 + 8 * cc));
+    }
+  }
 
   // ---- 1x128 row groups: token m0+tr+i, channels c0 .. c0+127 ----
 #pragma unroll
@@ -327,12 +388,16 @@ __global__ __launch_bounds__(T_THREADS) void quant_dual_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = quotient(v[i][e] * d.xmul, d.sc, d.r);
     const int64_t row = m0 + tr + i;
-    __builtin_nontemporal_store(u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])},
-                                reinterpret_cast<u32x2*>(xq + row * C + c0 + 8 * cc));
-    if (cc == 0) xs[row * (C / 128) + cb] = s;
+    if (row < a.M) {
+      __builtin_nontemporal_store(u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])},
+                                  reinterpret_cast<u32x2*>(a.xq + row * C + c0 + 8 * cc));
+      if (cc == 0) a.xs[row * (C / 128) + cb] = s;
+    }
   }
+  if (a.xq_t == nullptr) return;   // uniform over the workgroup
 
-  // ---- 128x1 token groups, written transposed ----
+  // ---- 128x1 token groups, written transposed (M % 128 == 0 here) ----
+  const int M = a.M;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float mm = 0.0f;
@@ -351,7 +416,7 @@ __global__ __launch_bounds__(T_THREADS) void quant_dual_kernel(
     p_sc[c] = d.sc;
     p_r[c] = d.r;
     p_mul[c] = d.xmul;
-    xs_t[(c0 + c) * (M / 128) + mb] = s;
+    a.xs_t[(c0 + c) * (M / 128) + mb] = s;
   }
   __syncthreads();
 #pragma unroll
@@ -370,11 +435,36 @@ __global__ __launch_bounds__(T_THREADS) void quant_dual_kernel(
     const int row = (t >> 3) + 32 * h;
     const int seg = t & 7;
     const uint8_t* src = tile + row * T_ROW_BYTES + 16 * seg;
-    const u32x2 a = *reinterpret_cast<const u32x2*>(src);
-    const u32x2 b = *reinterpret_cast<const u32x2*>(src + 8);
-    __builtin_nontemporal_store(u32x4{a[0], a[1], b[0], b[1]},
-                                reinterpret_cast<u32x4*>(xq_t + (c0 + row) * M + m0 + 16 * seg));
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
+    __builtin_nontemporal_store(u32x4{lo[0], lo[1], hi[0], hi[1]},
+                                reinterpret_cast<u32x4*>(a.xq_t + (c0 + row) * M + m0 + 16 * seg));
   }
+}
+
+// ============================================================================
+// RMSNorm statistics: rstd[m] = 1 / sqrt(fl32(sum_k x[m,k]^2 / K) + eps), one
+// wavefront per row. Each lane accumulates its 16-byte chunks in order with
+// fmaf; the 64 lane sums are added in a fixed butterfly, so the result is
+// deterministic.
+// ============================================================================
+__global__ __launch_bounds__(256) void rms_rstd_kernel(const uint16_t* __restrict__ x,
+                                                       float* __restrict__ rstd, int64_t M, int K,
+                                                       float eps, int64_t blk0) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (blk0 + blockIdx.x) * 4 + wave;
+  if (row >= M) return;   // uniform per wavefront
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + row * K);
+  float acc = 0.0f;
+  for (int c = lane; c < K / 8; c += 64) {
+    float v[8];
+    unpack8(__builtin_nontemporal_load(src + c), v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(v[e], v[e], acc);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) rstd[row] = 1.0f / sqrtf(acc / (float)K + eps);
 }
 
 // ============================================================================
@@ -431,16 +521,54 @@ hipError_t launch_transpose_quant_128x1(const void* x, int64_t M, int64_t C, uin
   return hipGetLastError();
 }
 
-hipError_t launch_quant_dual(const void* x, int64_t M, int64_t C, uint8_t* xq, float* xs,
-                             uint8_t* xq_t, float* xs_t, hipStream_t stream) {
+template <int OP>
+static hipError_t launch_ew(EwArgs a, int64_t M, int64_t C, hipStream_t stream) {
   const int64_t nc = C / T_CH;
   for (int64_t y0 = 0; y0 < nc; y0 += kMaxGridY) {
     const int64_t ny = nc - y0 < kMaxGridY ? nc - y0 : kMaxGridY;
-    hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)(M / 128), (unsigned)ny), dim3(T_THREADS), 0,
-                       stream, static_cast<const uint16_t*>(x), xq, xs, xq_t, xs_t, (int)M, (int)C,
-                       (int)y0);
+    a.cb0 = (int)y0;
+    hipLaunchKernelGGL(ew_quant_kernel<OP>, dim3((unsigned)((M + 127) / 128), (unsigned)ny), dim3(T_THREADS),
+                       0, stream, a);
   }
   return hipGetLastError();
+}
+
+static EwArgs ew_args(const void* x, int64_t M, int64_t C, uint8_t* xq, float* xs, uint8_t* xq_t,
+                      float* xs_t) {
+  EwArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.xq = xq; a.xs = xs; a.xq_t = xq_t; a.xs_t = xs_t;
+  a.M = (int)M; a.C = (int)C;
+  return a;
+}
+
+hipError_t launch_quant_dual(const void* x, int64_t M, int64_t C, uint8_t* xq, float* xs,
+                             uint8_t* xq_t, float* xs_t, hipStream_t stream) {
+  return launch_ew<EW_COPY>(ew_args(x, M, C, xq, xs, xq_t, xs_t), M, C, stream);
+}
+
+hipError_t launch_rmsnorm_quant(const void* x, const void* gamma, float eps, int64_t M, int64_t K,
+                                float* rstd, void* y, uint8_t* xq, float* xs, uint8_t* xq_t,
+                                float* xs_t, hipStream_t stream) {
+  const int64_t blocks = (M + 3) / 4;
+  for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocks1D) {
+    const int64_t nb = blocks - b0 < kMaxBlocks1D ? blocks - b0 : kMaxBlocks1D;
+    hipLaunchKernelGGL(rms_rstd_kernel, dim3((unsigned)nb), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), rstd, M, (int)K, eps, b0);
+  }
+  EwArgs a = ew_args(x, M, K, xq, xs, xq_t, xs_t);
+  a.gamma = static_cast<const uint16_t*>(gamma);
+  a.rstd = rstd;
+  a.y = static_cast<uint16_t*>(y);
+  return launch_ew<EW_RMSNORM>(a, M, K, stream);
+}
+
+hipError_t launch_swiglu_quant(const void* gate, const void* up, int64_t M, int64_t N, void* h,
+                               uint8_t* hq, float* hs, uint8_t* hq_t, float* hs_t, hipStream_t stream) {
+  EwArgs a = ew_args(gate, M, N, hq, hs, hq_t, hs_t);
+  a.x2 = static_cast<const uint16_t*>(up);
+  a.y = static_cast<uint16_t*>(h);
+  return launch_ew<EW_SWIGLU>(a, M, N, stream);
 }
 
 hipError_t launch_cast_f32_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define FP8BSQ_ABI_VERSION 2
+#define FP8BSQ_ABI_VERSION 3
 
 /* Status codes. */
 #define FP8BSQ_OK 0
@@ -56,6 +56,7 @@ extern "C" {
 #define FP8BSQ_ERR_SHAPE 2     /* a dimension is negative, too large or not a multiple of 128 where required */
 #define FP8BSQ_ERR_ALIGN 3     /* a pointer is not 16-byte aligned                    */
 #define FP8BSQ_ERR_HIP 4       /* the HIP runtime reported an error at launch         */
+#define FP8BSQ_ERR_VALUE 5     /* a scalar argument is out of range (eps must be finite and >= 0) */
 
 /* Returns a static, human-readable description of a status code. */
 const char* fp8bsq_strerror(int status);
@@ -122,6 +123,52 @@ int transpose_quantize_128x1(const void* x, int64_t M, int64_t C,
  */
 int quantize_dual_1x128_128x1(const void* x, int64_t M, int64_t K, uint8_t* xq, float* xs,
                               uint8_t* xq_t, float* xs_t, void* stream);
+
+/*
+ * rmsnorm_quantize_1x128 -- RMSNorm with the quantization of its output fused in.
+ * Source: "Esquema de Cuantización": the FP8 copy of an activation is made by
+ * the operator that produces it; "Implementación": quantization kernels fused
+ * with the RMSNorm operator.
+ *
+ *   x     in : bf16 [M, K]   (the residual stream)
+ *   gamma in : bf16 [K]
+ *   eps   in : float, finite, >= 0
+ *   rstd  out: fp32 [M]      rstd[m] = 1 / sqrt(fl32(sum_k x[m,k]^2 / K) + eps), the
+ *                            per-row statistic a backward pass needs (required)
+ *   y     out: bf16 [M, K] or NULL   y[m,k] = bf16(fl32(fl32(x[m,k] * rstd[m]) * gamma[k]))
+ *   xq, xs    out: quantize_act_1x128(y)
+ *   xq_t, xs_t out: transpose_quantize_128x1(y), or both NULL
+ * The codes are those of the bf16 values y, bit for bit, whether or not y is
+ * written. The sum of squares is accumulated in fp32 (per lane in order, then
+ * a fixed butterfly over the wavefront), so rstd is deterministic; y may
+ * differ from an exact evaluation by one bf16 unit in the last place.
+ * Shape: K % 128 == 0; M any (M % 128 == 0 when the transposed output is
+ * asked for). Two kernel launches (the row statistics, then the quantizing
+ * pass); rstd doubles as the buffer between them.
+ */
+int rmsnorm_quantize_1x128(const void* x, const void* gamma, float eps, int64_t M, int64_t K,
+                           float* rstd, void* y, uint8_t* xq, float* xs, uint8_t* xq_t, float* xs_t,
+                           void* stream);
+
+/*
+ * swiglu_quantize_1x128 -- the gated activation with the quantization of its
+ * output fused in (the down projection's input).
+ * Source: "Esquema de Cuantización" (FP8 copy made by the producing operator);
+ * "Implementación": quantization kernels fused with the activation operator.
+ *
+ *   gate, up in : bf16 [M, N]
+ *   h        out: bf16 [M, N] or NULL   h = bf16(fl32(silu(gate) * up)),
+ *                 silu(g) = fl32(g / fl32(1 + expf(-g)))
+ *   hq, hs     out: quantize_act_1x128(h)
+ *   hq_t, hs_t out: transpose_quantize_128x1(h), or both NULL
+ * The codes are those of the bf16 values h, bit for bit, whether or not h is
+ * written; h may differ from an exact evaluation by one bf16 unit in the last
+ * place (expf is not correctly rounded).
+ * Shape: N % 128 == 0; M any (M % 128 == 0 when the transposed output is
+ * asked for).
+ */
+int swiglu_quantize_1x128(const void* gate, const void* up, int64_t M, int64_t N, void* h,
+                          uint8_t* hq, float* hs, uint8_t* hq_t, float* hs_t, void* stream);
 
 /*
  * fp8_gemm_fwd -- forward / rollout GEMM, Y = Xq . Wq^T.

@@ -29,7 +29,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"quantize_act_1x128", "quantize_weight_128x128", "transpose_quantize_128x1",
-                          "quantize_dual_1x128_128x1", "fp8_gemm_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
+                          "quantize_dual_1x128_128x1", "rmsnorm_quantize_1x128", "swiglu_quantize_1x128",
+                          "fp8_gemm_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
                           "fp8bsq_strerror", "fp8bsq_abi_version", "fp8bsq_cast_f32_e4m3"}
     for n in names:
         assert hasattr(lib, n), n
@@ -37,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_strerror(lib):
     lib.fp8bsq_abi_version.restype = ctypes.c_int
-    assert lib.fp8bsq_abi_version() == 2
+    assert lib.fp8bsq_abi_version() == 3
     lib.fp8bsq_strerror.restype = ctypes.c_char_p
     lib.fp8bsq_strerror.argtypes = [ctypes.c_int]
     for code in range(5):
@@ -86,6 +87,32 @@ def test_dual_quantizer_validation(lib):
     assert d(FAKE, 128, 128, FAKE, FAKE, None, FAKE, None) == 1       # every output is required
     assert d(FAKE, 128, 128, FAKE, FAKE, FAKE, MISALIGNED, None) == 3
     assert d(None, 0, 128, None, None, None, None, None) == 0         # empty: no-op
+
+
+def test_fused_producer_validation(lib):
+    r = lib.rmsnorm_quantize_1x128
+    r.argtypes = [P, P, ctypes.c_float, I64, I64, P, P, P, P, P, P, P]
+    r.restype = ctypes.c_int
+    assert r(FAKE, FAKE, 1e-6, 3, 96, FAKE, None, FAKE, FAKE, None, None, None) == 2    # K % 128
+    assert r(FAKE, FAKE, 1e-6, 3, 128, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 2   # transposed needs M % 128
+    assert r(FAKE, FAKE, -1.0, 3, 128, FAKE, None, FAKE, FAKE, None, None, None) == 5   # eps < 0
+    assert r(FAKE, FAKE, float("nan"), 3, 128, FAKE, None, FAKE, FAKE, None, None, None) == 5
+    assert r(FAKE, FAKE, float("inf"), 3, 128, FAKE, None, FAKE, FAKE, None, None, None) == 5
+    assert r(FAKE, FAKE, 1e-6, 3, 128, None, None, FAKE, FAKE, None, None, None) == 1   # rstd required
+    assert r(FAKE, FAKE, 1e-6, 128, 128, FAKE, None, FAKE, FAKE, FAKE, None, None) == 1 # half of the transposed pair
+    assert r(FAKE, MISALIGNED, 1e-6, 3, 128, FAKE, None, FAKE, FAKE, None, None, None) == 3
+    assert r(None, None, 1e-6, 0, 128, None, None, None, None, None, None, None) == 0    # empty
+    w = lib.swiglu_quantize_1x128
+    w.argtypes = [P, P, I64, I64, P, P, P, P, P, P]
+    w.restype = ctypes.c_int
+    assert w(FAKE, FAKE, 5, 100, None, FAKE, FAKE, None, None, None) == 2
+    assert w(FAKE, FAKE, 5, 128, None, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert w(FAKE, None, 5, 128, None, FAKE, FAKE, None, None, None) == 1
+    assert w(FAKE, FAKE, 5, 128, MISALIGNED, FAKE, FAKE, None, None, None) == 3
+    assert w(None, None, 0, 128, None, None, None, None, None, None) == 0
+    lib.fp8bsq_strerror.restype = ctypes.c_char_p
+    lib.fp8bsq_strerror.argtypes = [ctypes.c_int]
+    assert b"out of range" in lib.fp8bsq_strerror(5)
 
 
 def test_gemm_validation(lib):
