@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-producers", action="store_true",
+                    help="skip timing the fused RMSNorm / SwiGLU producers (reported outside the step)")
     ap.add_argument("--separate-quant", action="store_true",
                     help="quantize X and dY with the single-output kernels (two reads each)")
     ap.add_argument("--traffic-from", default=None,
@@ -140,6 +142,50 @@ class Linear:
             L.append(("gemm_wgrad", f"{self.name}.wgrad[{N}x{K}x{M}]", 2 * M * N * K, M * N + M * K + 2 * N * K,
                       lambda: fq.fp8_gemm_wgrad(self.dyq_t, self.dys_t, self.xq_t, self.xs_t, out=self.dw)))
         return L
+
+
+def time_producers(fq, inputs, torch, wl, reps=10):
+    """The fused producers at the workload's shapes, timed outside the step.
+
+    RMSNorm of the hidden input [M, K] and SwiGLU of the intermediate [M, N]
+    (the up linear's width), each with both groupings quantized and no bf16
+    copy written. Algorithmic bytes: 2 B read per input element + 2 B of codes
+    + 8 B of scales per 128 elements (+ 4 B of rstd per row); the RMSNorm
+    implementation reads x twice (row statistics, then the quantizing pass).
+    """
+    lins = {l["name"]: l for l in wl["linears"]}
+    if "fwd" not in wl["passes"] or not ({"qkv", "up"} <= set(lins)):
+        return None
+    M, K, N = lins["qkv"]["M"], lins["qkv"]["K"], lins["up"]["N"]
+    x = inputs.bf16_normal_device((M, K), 1.0, 0.01, seed=41)
+    g = inputs.bf16_normal_device((K,), 0.5, 0.0, seed=42)
+    gate = inputs.bf16_normal_device((M, N), 2.0, 0.0, seed=43)
+    up = inputs.bf16_normal_device((M, N), 1.0, 0.0, seed=44)
+    out_r = fq.rmsnorm_quantize_1x128(x, g, 1e-6, True)
+    out_s = fq.swiglu_quantize_1x128(gate, up, True)
+    cases = [
+        (f"rmsnorm_quantize[{M},{K}]", M * K * 4 + M * K // 16 + M * 4,
+         lambda: fq.rmsnorm_quantize_1x128(x, g, 1e-6, True, False, *out_r[:5])),
+        (f"swiglu_quantize[{M},{N}]", M * N * 6 + M * N // 16,
+         lambda: fq.swiglu_quantize_1x128(gate, up, True, False, *out_s[:4])),
+    ]
+    res = {}
+    stream = torch.cuda.current_stream()
+    for key, nbytes, fn in cases:
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[key] = {"ms": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    del x, g, gate, up, out_r, out_s
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(inputs, wl, tokens=16384):
@@ -346,6 +392,10 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    if not args.no_producers:
+        prod = time_producers(fq, inputs, torch, wl)
+        if prod:
+            result["producers"] = prod
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inputs, wl)

@@ -287,7 +287,8 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
 // transposed (xq_t, xs_t; as transpose_quantize_128x1). The producer is
 //   EW_COPY     the input itself (the dual quantizer);
 //   EW_RMSNORM  y = bf16(fl32(fl32(x * rstd[m]) * gamma[c]));
-//   EW_SWIGLU   y = bf16(fl32(silu(g) * u)), silu(g) = fl32(g / fl32(1 + expf(-g))).
+//   EW_SWIGLU   y = bf16(fl32(silu(g) * u)), silu(g) = g * rcp(1 + exp2(-g * log2(e)))
+//               with the hardware exp2 and reciprocal (relative error ~2^-21).
 // Thread layout and the transposed half are those of the 128x1 kernel; a row
 // group's amax is this thread's 8 channels reduced over the 16 lanes that
 // share its 8 tokens (one DPP row). Without the transposed output M may be
@@ -358,7 +359,10 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
       unpack8(raw2[i], uv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float sg = gv[e] / (1.0f + expf(-gv[e]));
+        // sigmoid with the hardware exp2 and reciprocal (each within ~1 ulp):
+        // exp(-g) overflowing to inf gives g * 0 = -0 for very negative g
+        const float ex = __builtin_amdgcn_exp2f(gv[e] * -1.44269504088896341f);
+        const float sg = gv[e] * __builtin_amdgcn_rcpf(1.0f + ex);
         v[i][e] = round_bf16(sg * uv[e]);
       }
     }

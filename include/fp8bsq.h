@@ -157,13 +157,14 @@ int rmsnorm_quantize_1x128(const void* x, const void* gamma, float eps, int64_t 
  * "Implementación": quantization kernels fused with the activation operator.
  *
  *   gate, up in : bf16 [M, N]
- *   h        out: bf16 [M, N] or NULL   h = bf16(fl32(silu(gate) * up)),
- *                 silu(g) = fl32(g / fl32(1 + expf(-g)))
+ *   h        out: bf16 [M, N] or NULL   h = bf16(fl32(silu(gate) * up)), with
+ *                 silu(g) = g * sigmoid(g) evaluated in fp32 from the hardware
+ *                 exp2 and reciprocal (relative error about 2^-21)
  *   hq, hs     out: quantize_act_1x128(h)
  *   hq_t, hs_t out: transpose_quantize_128x1(h), or both NULL
  * The codes are those of the bf16 values h, bit for bit, whether or not h is
  * written; h may differ from an exact evaluation by one bf16 unit in the last
- * place (expf is not correctly rounded).
+ * place.
  * Shape: N % 128 == 0; M any (M % 128 == 0 when the transposed output is
  * asked for).
  */
