@@ -1,0 +1,106 @@
+"""FP8Linear: the unified FP8 flow of one linear layer as a torch autograd op.
+
+Source: Resumen Técnico: Jet-RL (gist.science). "Arquitectura Central": the
+bf16 master weights are quantized for use, and rollout (inference) and the
+training forward run one and the same quantization flow, so the inference
+graph is a subgraph of the training forward graph. "Esquema de
+Cuantización": the linear layers are FP8 GEMMs on 1x128 activation groups and
+128x128 weight blocks; DGrad and WGrad run in FP8 (WGrad on 1x128 / 128x1
+groupings); the activations kept for the backward pass are stored in FP8.
+
+Every step runs in the library's HIP kernels through the C ABI:
+    forward   quantize_weight_128x128(W)         once per weight version (cached)
+              quantize_dual_1x128_128x1(X)        training: X codes for the GEMM and
+                                                  the transposed codes saved for WGrad
+              quantize_act_1x128(X)               inference (gradients off or not needed)
+              fp8_gemm_fwd                        Y = Xq Wq^T
+    backward  quantize_dual_1x128_128x1(dY)
+              fp8_gemm_dgrad                      dX = dYq Wq
+              fp8_gemm_wgrad                      dW = dYq^T Xq
+Both paths quantize X with the same 1x128 rule and call the same GEMM, so a
+row of Y does not depend on whether gradients are tracked, on the other rows
+of the batch, or on the batch size.
+"""
+
+import torch
+
+from . import (fp8_gemm_dgrad, fp8_gemm_fwd, fp8_gemm_wgrad, quantize_act_1x128,
+               quantize_dual_1x128_128x1, quantize_weight_128x128)
+
+
+class _WeightCodes:
+    """FP8 codes of a bf16 weight, refreshed when the weight changes in place."""
+
+    def __init__(self):
+        self.key = None
+        self.wq = self.ws = self.wq_t = None
+
+    def get(self, w):
+        key = (w.data_ptr(), w._version, tuple(w.shape))
+        if key != self.key:
+            self.wq, self.ws, self.wq_t = quantize_weight_128x128(w.detach(), transposed=True)
+            self.key = key
+        return self.wq, self.ws, self.wq_t
+
+
+class FP8LinearFunction(torch.autograd.Function):
+    """Y = X W^T with FP8 block-scaled operands; X [M, K] and W [N, K] in bf16."""
+
+    @staticmethod
+    def forward(ctx, x, w, codes):
+        if x.shape[0] % 128:
+            raise ValueError("training needs the token count to be a multiple of 128 "
+                             "(WGrad groups the tokens by 128)")
+        wq, ws, wq_t = codes.get(w)
+        xq, xs, xq_t, xs_t = quantize_dual_1x128_128x1(x)
+        y = fp8_gemm_fwd(xq, xs, wq, ws)
+        ctx.save_for_backward(xq_t, xs_t, wq_t, ws)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        xq_t, xs_t, wq_t, ws = ctx.saved_tensors
+        dy = dy.contiguous()
+        need_dx, need_dw = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if need_dw:
+            dyq, dys, dyq_t, dys_t = quantize_dual_1x128_128x1(dy)
+        else:
+            dyq, dys = quantize_act_1x128(dy)
+        dx = fp8_gemm_dgrad(dyq, dys, wq_t, ws) if need_dx else None
+        dw = fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t) if need_dw else None
+        return dx, dw, None
+
+
+def fp8_linear_inference(x, w, codes):
+    """The rollout path: Y = Xq Wq^T with no state kept for a backward pass."""
+    wq, ws, _ = codes.get(w)
+    xq, xs = quantize_act_1x128(x)
+    return fp8_gemm_fwd(xq, xs, wq, ws)
+
+
+class FP8Linear(torch.nn.Module):
+    """A bias-free linear layer (in_features -> out_features) on the FP8 flow.
+
+    The weight is a bf16 parameter [out_features, in_features]; both feature
+    counts must be multiples of 128. Inputs are bf16 [..., in_features] on the
+    GPU; leading dimensions are flattened into tokens.
+    """
+
+    def __init__(self, in_features, out_features, device="cuda", weight=None):
+        super().__init__()
+        if in_features % 128 or out_features % 128:
+            raise ValueError("in_features and out_features must be multiples of 128")
+        if weight is None:
+            weight = torch.empty((out_features, in_features), dtype=torch.bfloat16, device=device)
+            torch.nn.init.normal_(weight, std=0.02)
+        self.weight = torch.nn.Parameter(weight)
+        self._codes = _WeightCodes()
+
+    def forward(self, x):
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, x.shape[-1]).contiguous()
+        if torch.is_grad_enabled() and (self.weight.requires_grad or x2.requires_grad):
+            y = FP8LinearFunction.apply(x2, self.weight, self._codes)
+        else:
+            y = fp8_linear_inference(x2, self.weight, self._codes)
+        return y.reshape(*lead, y.shape[-1])
