@@ -286,8 +286,8 @@ def main():
         summarize_counters(args.summarize_counters)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is "
-              "described in DESIGN.md and not measured here.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); a multi-GPU layout "
+              "is not measured here.", file=sys.stderr)
         sys.exit(2)
 
     import torch
