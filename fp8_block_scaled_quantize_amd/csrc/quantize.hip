@@ -309,8 +309,6 @@ struct EwArgs {
   int M, C, cb0;
 };
 
-__device__ __forceinline__ float round_bf16(float v) { return __uint_as_float(f32_to_bf16_rne(v) << 16); }
-
 template <int OP>
 __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
   __shared__ float red[4][T_CH];
@@ -336,25 +334,30 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
       raw2[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x2 + row * C + c0 + 8 * cc));
   }
 
-  float v[8][8];
+  // The produced values are bf16 numbers; they stay packed (two per
+  // register) and are widened where used, which halves the registers held
+  // across the two quantizing passes.
+  u32x4 pv[8];
   if (OP == EW_COPY) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) unpack8(raw[i], v[i]);
+    for (int i = 0; i < 8; ++i) pv[i] = raw[i];
   } else if (OP == EW_RMSNORM) {
     float gm[8];
     unpack8(*reinterpret_cast<const u32x4*>(a.gamma + c0 + 8 * cc), gm);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float r = a.rstd[min(m0 + tr + i, (int64_t)a.M - 1)];
-      float xv[8];
+      float xv[8], yv[8];
       unpack8(raw[i], xv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[i][e] = round_bf16((xv[e] * r) * gm[e]);
+      for (int e = 0; e < 8; ++e) yv[e] = (xv[e] * r) * gm[e];
+      pv[i] = u32x4{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
+                    pack_bf16x2(yv[6], yv[7])};
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float gv[8], uv[8];
+      float gv[8], uv[8], yv[8];
       unpack8(raw[i], gv);
       unpack8(raw2[i], uv);
 #pragma unroll
@@ -363,19 +366,21 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
         // exp(-g) overflowing to inf gives g * 0 = -0 for very negative g
         const float ex = __builtin_amdgcn_exp2f(gv[e] * -1.44269504088896341f);
         const float sg = gv[e] * __builtin_amdgcn_rcpf(1.0f + ex);
-        v[i][e] = round_bf16(sg * uv[e]);
+        yv[e] = sg * uv[e];
       }
+      pv[i] = u32x4{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
+                    pack_bf16x2(yv[6], yv[7])};
     }
   }
+  auto val = [&](int i, int e) -> float {
+    const uint32_t w = pv[i][e >> 1];
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+  };
   if (OP != EW_COPY && a.y != nullptr) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t row = m0 + tr + i;
-      if (row < a.M)
-        __builtin_nontemporal_store(
-            u32x4{pack_bf16x2(v[i][0], v[i][1]), pack_bf16x2(v[i][2], v[i][3]),
-                  pack_bf16x2(v[i][4], v[i][5]), pack_bf16x2(v[i][6], v[i][7])},
-            reinterpret_cast<u32x4*>(a.y + row * C + c0 + 8 * cc));
+      if (row < a.M) __builtin_nontemporal_store(pv[i], reinterpret_cast<u32x4*>(a.y + row * C + c0 + 8 * cc));
     }
   }
 
@@ -384,13 +389,13 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
   for (int i = 0; i < 8; ++i) {
     float m = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[i][e]));
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(val(i, e)));
     m = max16(m);
     const float s = group_scale(m);
     const GroupDiv d = group_div(m, s);
     float q[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = quotient(v[i][e] * d.xmul, d.sc, d.r);
+    for (int e = 0; e < 8; ++e) q[e] = quotient(val(i, e) * d.xmul, d.sc, d.r);
     const int64_t row = m0 + tr + i;
     if (row < a.M) {
       __builtin_nontemporal_store(u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])},
@@ -406,7 +411,7 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
   for (int e = 0; e < 8; ++e) {
     float mm = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) mm = fmaxf(mm, fabsf(v[i][e]));
+    for (int i = 0; i < 8; ++i) mm = fmaxf(mm, fabsf(val(i, e)));
     mm = fmaxf(mm, __shfl_xor(mm, 16, 64));
     mm = fmaxf(mm, __shfl_xor(mm, 32, 64));
     if (lane < 16) red[wave][8 * lane + e] = mm;
@@ -429,7 +434,7 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
     const float sc = p_sc[c], r = p_r[c], mul = p_mul[c];
     float q[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = quotient(v[i][e] * mul, sc, r);
+    for (int i = 0; i < 8; ++i) q[i] = quotient(val(i, e) * mul, sc, r);
     *reinterpret_cast<u32x2*>(tile + c * T_ROW_BYTES + tr) =
         u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
   }
