@@ -29,6 +29,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace fp8bsq {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -291,6 +293,14 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
     ccarry[b] = 0.0f;
   }
   f32x4 rprev = zero;
+  // The loop body is instantiated twice: with 8 wavefronts, the second
+  // wavefront of each SIMD (waves 4-7) issues its copies one slice later than
+  // the first, so the two do not stall on copy issue at the same moments
+  // (+4 % on WGrad, neutral elsewhere). The offset is a compile-time
+  // constant so the unrolled slices stay free of branches.
+  constexpr int LOAD_SLICES_ = 4;   // slices over which a step's copies are spread
+  auto main_loop = [&](auto copy_offset) {
+  constexpr int OFF = decltype(copy_offset)::value;
   int st = 0;                       // stage of step kb
   for (int kb = 0; kb < p.Kb; ++kb) {
     const uint8_t* tp = tiles[st];
@@ -322,15 +332,16 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
     const int kn = min(kb + NST - 1, p.Kb - 1);
     const int sn = st == 0 ? NST - 1 : st - 1;    // stage of step kb + NST - 1 (idle now)
     load_blk_scales(kn, sn);
-    constexpr int LOAD_SLICES = 4;
-    static_assert(P_INSTR % LOAD_SLICES == 0 && Q_INSTR % LOAD_SLICES == 0 && SI >= LOAD_SLICES, "load spread");
+    constexpr int LOAD_SLICES = LOAD_SLICES_;
+    static_assert(P_INSTR % LOAD_SLICES == 0 && Q_INSTR % LOAD_SLICES == 0 && SI >= LOAD_SLICES + OFF, "load spread");
 #pragma unroll
     for (int a = 0; a < SI; ++a) {
-      if (a < LOAD_SLICES) {
+      if (a >= OFF && a < OFF + LOAD_SLICES) {
+        const int al = a - OFF;
 #pragma unroll
-        for (int r = 0; r < P_INSTR / LOAD_SLICES; ++r) p_slab(a * (P_INSTR / LOAD_SLICES) + r, kn, sn);
+        for (int r = 0; r < P_INSTR / LOAD_SLICES; ++r) p_slab(al * (P_INSTR / LOAD_SLICES) + r, kn, sn);
 #pragma unroll
-        for (int r = 0; r < Q_INSTR / LOAD_SLICES; ++r) q_slab(a * (Q_INSTR / LOAD_SLICES) + r, kn, sn);
+        for (int r = 0; r < Q_INSTR / LOAD_SLICES; ++r) q_slab(al * (Q_INSTR / LOAD_SLICES) + r, kn, sn);
       }
       const i32x8 pf = a == 0 ? pf0 : load_frag(tp, wi * C::WI + a * 16 + r16);
       f32x4 rs = zero;
@@ -373,6 +384,12 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
     __syncthreads();
     st = st + 1 == NST ? 0 : st + 1;
   }
+  };
+  constexpr int OFF_HI = (C::NT == 512 && SI >= LOAD_SLICES_ + 1) ? 1 : 0;
+  if (OFF_HI && wave >= 4)
+    main_loop(std::integral_constant<int, OFF_HI>{});
+  else
+    main_loop(std::integral_constant<int, 0>{});
   if (CARRY) {
 #pragma unroll
     for (int b = 0; b < SJ; ++b) promote1(acc[SI - 1][b], dprev[b], ccarry[b], rprev);
