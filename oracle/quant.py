@@ -112,14 +112,20 @@ def transpose_quantize_128x1(x_bits):
     Each group is 128 consecutive tokens of one channel, i.e. it runs along
     the token dimension, which is WGrad's contraction dimension.
 
-    Returns xq_t uint8 [C, M] and xs_t float32 [C, M/128]; xs_t[c, b] is the
-    scale of x[128b : 128b + 128, c], and xq_t[c, m] is the code of x[m, c].
+    Any token count M is accepted. With Mp = 128 * ceil(M / 128), returns
+    xq_t uint8 [C, Mp] and xs_t float32 [C, Mp/128]: xq_t[c, m] is the code of
+    x[m, c] and xs_t[c, b] the scale of the group x[128b : min(128b + 128, M), c].
+    When M is not a multiple of 128 the last group holds the remaining tokens
+    (its amax is theirs) and the positions m >= M hold code 0x00 (+0), which a
+    contraction over the tokens reads as zero products. (Reading: the pages
+    fix no layout for a ragged tail; padding the transposed copy keeps WGrad's
+    contraction a whole number of 128-token blocks.)
     """
     x = bf16_bits_to_f32(x_bits)
     M, C = x.shape
-    if M % GROUP:
-        raise ValueError("M must be a multiple of 128")
-    Mb = M // GROUP
-    xt = np.ascontiguousarray(x.T)                      # [C, M]
+    Mb = (M + GROUP - 1) // GROUP
+    Mp = Mb * GROUP
+    xt = np.zeros((C, Mp), dtype=np.float32)            # +0 beyond the last token
+    xt[:, :M] = x.T
     q, s = _grouped_scales_and_codes(xt.reshape(C * Mb, GROUP))
-    return q.reshape(C, M), s.reshape(C, Mb)
+    return q.reshape(C, Mp), s.reshape(C, Mb)

@@ -191,6 +191,29 @@ def test_transpose_identities():
     assert np.array_equal(wq2_t, wq)
 
 
+@pytest.mark.parametrize("M", [1, 100, 127, 129, 300])
+def test_transpose_ragged_token_count(M):
+    # A tail of fewer than 128 tokens: per channel, the group of the remaining
+    # tokens is quantized on its own (exact rationals + brute-force rounding)
+    # and the padded positions hold +0 codes.
+    x = _llama_like(M, 256, seed=M)
+    qt, st = quant.transpose_quantize_128x1(x)
+    Mp = -(-M // 128) * 128
+    assert qt.shape == (256, Mp) and st.shape == (256, Mp // 128)
+    assert np.all(qt[:, M:] == 0)
+    xf = e4m3.bf16_bits_to_f32(x)
+    for c in (0, 77, 255):
+        for b in range(Mp // 128):
+            vals = xf[128 * b:min(128 * b + 128, M), c]
+            sc, codes = _exact_group(vals)
+            assert float(st[c, b]) == float(sc)
+            assert list(qt[c, 128 * b:128 * b + len(vals)]) == codes
+    if M > 128:                       # the whole groups agree with the 1x128 rule on X^T
+        full = (M // 128) * 128
+        q1, s1 = quant.quantize_act_1x128(np.ascontiguousarray(x[:full].T))
+        assert np.array_equal(qt[:, :full], q1) and np.array_equal(st[:, :full // 128], s1)
+
+
 # -------------------------------------------------------- independent impl --
 
 def test_matches_torch_pipeline():
