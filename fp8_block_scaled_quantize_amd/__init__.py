@@ -12,7 +12,7 @@ Entry points (same names as the C ABI):
     quantize_act_1x128(x)             -> (xq [M,K] uint8, xs [M,K/128] float32)
     quantize_weight_128x128(w, transposed=True)
                                       -> (wq [N,K], ws [N/128,K/128], wq_t [K,N] or None)
-    transpose_quantize_128x1(x)       -> (xq_t [C,M], xs_t [C,M/128])
+    transpose_quantize_128x1(x)       -> (xq_t [C,Mp], xs_t [C,Mp/128]), Mp = M rounded up to 128
     quantize_dual_1x128_128x1(x)      -> (xq, xs, xq_t, xs_t): both of the above, one read of x
     rmsnorm_quantize_1x128(x, gamma, eps, transposed=False, write_y=False)
                                       -> (xq, xs, xq_t, xs_t, rstd, y): RMSNorm, its output quantized
@@ -149,12 +149,18 @@ def quantize_weight_128x128(w, transposed=True, wq=None, ws=None, wq_t=None):
     return wq, ws, wq_t
 
 
+def padded_tokens(M):
+    """Token length of the 128x1 (transposed) outputs: M rounded up to 128."""
+    return (M + 127) // 128 * 128
+
+
 def transpose_quantize_128x1(x, xq_t=None, xs_t=None):
     import torch
     M, C = x.shape
+    Mp = padded_tokens(M)
     _need(x, "x", torch.bfloat16, (M, C))
-    xq_t = _out(xq_t, "xq_t", torch.uint8, (C, M), x)
-    xs_t = _out(xs_t, "xs_t", torch.float32, (C, M // 128), x)
+    xq_t = _out(xq_t, "xq_t", torch.uint8, (C, Mp), x)
+    xs_t = _out(xs_t, "xs_t", torch.float32, (C, Mp // 128), x)
     _check("transpose_quantize_128x1", load_library().transpose_quantize_128x1(
         _ptr(x), M, C, _ptr(xq_t), _ptr(xs_t), _stream(x)))
     return xq_t, xs_t
@@ -166,8 +172,9 @@ def quantize_dual_1x128_128x1(x, xq=None, xs=None, xq_t=None, xs_t=None):
     _need(x, "x", torch.bfloat16, (M, K))
     xq = _out(xq, "xq", torch.uint8, (M, K), x)
     xs = _out(xs, "xs", torch.float32, (M, K // 128), x)
-    xq_t = _out(xq_t, "xq_t", torch.uint8, (K, M), x)
-    xs_t = _out(xs_t, "xs_t", torch.float32, (K, M // 128), x)
+    Mp = padded_tokens(M)
+    xq_t = _out(xq_t, "xq_t", torch.uint8, (K, Mp), x)
+    xs_t = _out(xs_t, "xs_t", torch.float32, (K, Mp // 128), x)
     _check("quantize_dual_1x128_128x1", load_library().quantize_dual_1x128_128x1(
         _ptr(x), M, K, _ptr(xq), _ptr(xs), _ptr(xq_t), _ptr(xs_t), _stream(x)))
     return xq, xs, xq_t, xs_t
@@ -183,8 +190,8 @@ def rmsnorm_quantize_1x128(x, gamma, eps=1e-6, transposed=False, write_y=False,
     xs = _out(xs, "xs", torch.float32, (M, K // 128), x)
     rstd = _out(rstd, "rstd", torch.float32, (M,), x)
     if transposed:
-        xq_t = _out(xq_t, "xq_t", torch.uint8, (K, M), x)
-        xs_t = _out(xs_t, "xs_t", torch.float32, (K, M // 128), x)
+        xq_t = _out(xq_t, "xq_t", torch.uint8, (K, padded_tokens(M)), x)
+        xs_t = _out(xs_t, "xs_t", torch.float32, (K, padded_tokens(M) // 128), x)
     else:
         xq_t = xs_t = None
     y = _out(y, "y", torch.bfloat16, (M, K), x) if write_y else None
@@ -203,8 +210,8 @@ def swiglu_quantize_1x128(gate, up, transposed=False, write_h=False,
     hq = _out(hq, "hq", torch.uint8, (M, N), gate)
     hs = _out(hs, "hs", torch.float32, (M, N // 128), gate)
     if transposed:
-        hq_t = _out(hq_t, "hq_t", torch.uint8, (N, M), gate)
-        hs_t = _out(hs_t, "hs_t", torch.float32, (N, M // 128), gate)
+        hq_t = _out(hq_t, "hq_t", torch.uint8, (N, padded_tokens(M)), gate)
+        hs_t = _out(hs_t, "hs_t", torch.float32, (N, padded_tokens(M) // 128), gate)
     else:
         hq_t = hs_t = None
     h = _out(h, "h", torch.bfloat16, (M, N), gate) if write_h else None

@@ -22,6 +22,10 @@ bool dims_ok(int64_t a, int64_t b) {
   return a == 0 || b < kMaxElems / a;
 }
 
+// Token count rounded up to a whole 128-token block: the token length of the
+// transposed (128x1) outputs.
+int64_t round128(int64_t m) { return (m + 127) / 128 * 128; }
+
 int hip_status(hipError_t e) { return e == hipSuccess ? FP8BSQ_OK : FP8BSQ_ERR_HIP; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -64,7 +68,7 @@ int quantize_weight_128x128(const void* w, int64_t N, int64_t K, uint8_t* wq, fl
 
 int transpose_quantize_128x1(const void* x, int64_t M, int64_t C, uint8_t* xq_t, float* xs_t,
                              void* stream) {
-  if (!dims_ok(M, C) || M % 128 || C % 128) return FP8BSQ_ERR_SHAPE;
+  if (!dims_ok(M, C) || !dims_ok(round128(M), C) || C % 128) return FP8BSQ_ERR_SHAPE;
   if (M == 0 || C == 0) return FP8BSQ_OK;
   if (!x || !xq_t || !xs_t) return FP8BSQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(xq_t) || !aligned16(xs_t)) return FP8BSQ_ERR_ALIGN;
@@ -73,7 +77,7 @@ int transpose_quantize_128x1(const void* x, int64_t M, int64_t C, uint8_t* xq_t,
 
 int quantize_dual_1x128_128x1(const void* x, int64_t M, int64_t K, uint8_t* xq, float* xs,
                               uint8_t* xq_t, float* xs_t, void* stream) {
-  if (!dims_ok(M, K) || M % 128 || K % 128) return FP8BSQ_ERR_SHAPE;
+  if (!dims_ok(M, K) || !dims_ok(round128(M), K) || K % 128) return FP8BSQ_ERR_SHAPE;
   if (M == 0 || K == 0) return FP8BSQ_OK;
   if (!x || !xq || !xs || !xq_t || !xs_t) return FP8BSQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(xq) || !aligned16(xs) || !aligned16(xq_t) || !aligned16(xs_t))
@@ -85,7 +89,7 @@ int rmsnorm_quantize_1x128(const void* x, const void* gamma, float eps, int64_t 
                            float* rstd, void* y, uint8_t* xq, float* xs, uint8_t* xq_t, float* xs_t,
                            void* stream) {
   const bool tr = xq_t != nullptr || xs_t != nullptr;
-  if (!dims_ok(M, K) || K % 128 || (tr && M % 128)) return FP8BSQ_ERR_SHAPE;
+  if (!dims_ok(M, K) || !dims_ok(round128(M), K) || K % 128) return FP8BSQ_ERR_SHAPE;
   if (!(eps >= 0.0f) || eps == INFINITY) return FP8BSQ_ERR_VALUE;
   if (M == 0 || K == 0) return FP8BSQ_OK;
   if (!x || !gamma || !rstd || !xq || !xs || (tr && (!xq_t || !xs_t))) return FP8BSQ_ERR_NULL;
@@ -99,7 +103,7 @@ int rmsnorm_quantize_1x128(const void* x, const void* gamma, float eps, int64_t 
 int swiglu_quantize_1x128(const void* gate, const void* up, int64_t M, int64_t N, void* h,
                           uint8_t* hq, float* hs, uint8_t* hq_t, float* hs_t, void* stream) {
   const bool tr = hq_t != nullptr || hs_t != nullptr;
-  if (!dims_ok(M, N) || N % 128 || (tr && M % 128)) return FP8BSQ_ERR_SHAPE;
+  if (!dims_ok(M, N) || !dims_ok(round128(M), N) || N % 128) return FP8BSQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BSQ_OK;
   if (!gate || !up || !hq || !hs || (tr && (!hq_t || !hs_t))) return FP8BSQ_ERR_NULL;
   if (!aligned16(gate) || !aligned16(up) || !aligned16(hq) || !aligned16(hs) || (h && !aligned16(h)) ||

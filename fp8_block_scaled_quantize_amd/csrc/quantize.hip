@@ -202,7 +202,8 @@ __global__ __launch_bounds__(W_THREADS) void quant_weight_128x128_kernel(
 // tokens, across the 4 lanes of a wavefront that share the channels, then
 // across the 4 wavefronts through LDS. The codes go to an LDS tile
 // [128 channels][128 tokens] as 8-byte pieces and leave as 128-byte rows of
-// xq_t.
+// xq_t. A ragged token count M is padded: xq_t is [C, Mp] with Mp = M rounded
+// up to 128, and the tokens past M are read as +0 (code 0x00).
 // ============================================================================
 constexpr int T_THREADS = 256;
 constexpr int T_CH = 128;
@@ -222,12 +223,18 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
   const int mb = blockIdx.x;
   const int64_t m0 = (int64_t)mb * 128;
   const int64_t c0 = ((int64_t)cb0 + blockIdx.y) * T_CH;
+  const int64_t Mp = ((int64_t)M + 127) & ~(int64_t)127;   // padded token count of xq_t
 
+  // tokens past M (a ragged last block) read as +0: they leave the amax
+  // alone and quantize to code 0x00
   u32x4 raw[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = m0 + tr + i;
     raw[i] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(x + (m0 + tr + i) * C + c0 + 8 * cc));
+        reinterpret_cast<const u32x4*>(x + min(row, (int64_t)M - 1) * C + c0 + 8 * cc));
+    if (row >= M) raw[i] = u32x4{0u, 0u, 0u, 0u};
+  }
 
   float v[8][8];
 #pragma unroll
@@ -251,7 +258,7 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
     p_sc[c] = d.sc;
     p_r[c] = d.r;
     p_mul[c] = d.xmul;
-    xs_t[(c0 + c) * (M / 128) + mb] = s;
+    xs_t[(c0 + c) * (Mp / 128) + mb] = s;
   }
   __syncthreads();
 
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
     const u32x2 a = *reinterpret_cast<const u32x2*>(src);
     const u32x2 b = *reinterpret_cast<const u32x2*>(src + 8);
     __builtin_nontemporal_store(u32x4{a[0], a[1], b[0], b[1]},
-                                reinterpret_cast<u32x4*>(xq_t + (c0 + row) * M + m0 + 16 * seg));
+                                reinterpret_cast<u32x4*>(xq_t + (c0 + row) * Mp + m0 + 16 * seg));
   }
 }
 
@@ -291,8 +298,9 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
 //               with the hardware exp2 and reciprocal (relative error ~2^-21).
 // Thread layout and the transposed half are those of the 128x1 kernel; a row
 // group's amax is this thread's 8 channels reduced over the 16 lanes that
-// share its 8 tokens (one DPP row). Without the transposed output M may be
-// ragged: rows past M are read clamped and never stored.
+// share its 8 tokens (one DPP row). M may be ragged: rows past M are read
+// clamped, produce +0, and only the padded transposed copy [C, Mp] (Mp = M
+// rounded up to 128) holds their 0x00 codes.
 // ============================================================================
 enum EwOp { EW_COPY = 0, EW_RMSNORM = 1, EW_SWIGLU = 2 };
 
@@ -372,6 +380,11 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
                     pack_bf16x2(yv[6], yv[7])};
     }
   }
+  // tokens past M (a ragged last block) are +0: they leave the 128x1 amax
+  // alone and quantize to code 0x00 in the padded transposed copy
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (m0 + tr + i >= a.M) pv[i] = u32x4{0u, 0u, 0u, 0u};
   auto val = [&](int i, int e) -> float {
     const uint32_t w = pv[i][e >> 1];
     return (e & 1) ? bf16_hi(w) : bf16_lo(w);
@@ -405,8 +418,8 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
   }
   if (a.xq_t == nullptr) return;   // uniform over the workgroup
 
-  // ---- 128x1 token groups, written transposed (M % 128 == 0 here) ----
-  const int M = a.M;
+  // ---- 128x1 token groups, written transposed into [C, Mp] ----
+  const int64_t Mp = ((int64_t)a.M + 127) & ~(int64_t)127;   // padded token count of xq_t
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float mm = 0.0f;
@@ -425,7 +438,7 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
     p_sc[c] = d.sc;
     p_r[c] = d.r;
     p_mul[c] = d.xmul;
-    a.xs_t[(c0 + c) * (M / 128) + mb] = s;
+    a.xs_t[(c0 + c) * (Mp / 128) + mb] = s;
   }
   __syncthreads();
 #pragma unroll
@@ -447,7 +460,7 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
     const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
     const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
     __builtin_nontemporal_store(u32x4{lo[0], lo[1], hi[0], hi[1]},
-                                reinterpret_cast<u32x4*>(a.xq_t + (c0 + row) * M + m0 + 16 * seg));
+                                reinterpret_cast<u32x4*>(a.xq_t + (c0 + row) * Mp + m0 + 16 * seg));
   }
 }
 
@@ -523,7 +536,7 @@ hipError_t launch_transpose_quant_128x1(const void* x, int64_t M, int64_t C, uin
   const int64_t nc = C / T_CH;
   for (int64_t y0 = 0; y0 < nc; y0 += kMaxGridY) {
     const int64_t ny = nc - y0 < kMaxGridY ? nc - y0 : kMaxGridY;
-    hipLaunchKernelGGL(transpose_quant_128x1_kernel, dim3((unsigned)(M / 128), (unsigned)ny),
+    hipLaunchKernelGGL(transpose_quant_128x1_kernel, dim3((unsigned)((M + 127) / 128), (unsigned)ny),
                        dim3(T_THREADS), 0, stream, static_cast<const uint16_t*>(x), xq_t, xs_t,
                        (int)M, (int)C, (int)y0);
   }

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define FP8BSQ_ABI_VERSION 3
+#define FP8BSQ_ABI_VERSION 4
 
 /* Status codes. */
 #define FP8BSQ_OK 0
@@ -98,10 +98,13 @@ int quantize_weight_128x128(const void* w, int64_t N, int64_t K,
  * 1x128 / 128x1 operand groups; activations saved for backward are FP8.
  *
  *   x    in : bf16 [M, C]
- *   xq_t out: E4M3 [C, M]          xq_t[c, m] = code of x[m, c]
- *   xs_t out: fp32 [C, M/128]      xs_t[c, b] = scale of x[128b : 128b+128, c]
- * Bit-identical to quantize_act_1x128 applied to the transpose of x.
- * Shape: M % 128 == 0, C % 128 == 0.
+ *   xq_t out: E4M3 [C, Mp]         xq_t[c, m] = code of x[m, c]; Mp = M rounded up to 128
+ *   xs_t out: fp32 [C, Mp/128]     xs_t[c, b] = scale of x[128b : min(128b+128, M), c]
+ * For M % 128 == 0 (Mp = M), bit-identical to quantize_act_1x128 applied to
+ * the transpose of x. A ragged M: the last group holds the remaining tokens
+ * (its amax is theirs) and xq_t[c, m] = 0x00 (+0) for M <= m < Mp, so WGrad
+ * can contract over Mp tokens. (The pages fix no layout for a ragged tail.)
+ * Shape: C % 128 == 0; M any.
  */
 int transpose_quantize_128x1(const void* x, int64_t M, int64_t C,
                              uint8_t* xq_t, float* xs_t, void* stream);
@@ -117,9 +120,10 @@ int transpose_quantize_128x1(const void* x, int64_t M, int64_t C,
  *
  *   x    in : bf16 [M, K]
  *   xq   out: E4M3 [M, K],    xs   out: fp32 [M, K/128]   (as quantize_act_1x128)
- *   xq_t out: E4M3 [K, M],    xs_t out: fp32 [K, M/128]   (as transpose_quantize_128x1)
+ *   xq_t out: E4M3 [K, Mp],   xs_t out: fp32 [K, Mp/128]  (as transpose_quantize_128x1;
+ *                                                          Mp = M rounded up to 128)
  * Every output is bit-identical to the corresponding single-output call.
- * Shape: M % 128 == 0, K % 128 == 0.
+ * Shape: K % 128 == 0; M any.
  */
 int quantize_dual_1x128_128x1(const void* x, int64_t M, int64_t K, uint8_t* xq, float* xs,
                               uint8_t* xq_t, float* xs_t, void* stream);
@@ -142,8 +146,8 @@ int quantize_dual_1x128_128x1(const void* x, int64_t M, int64_t K, uint8_t* xq, 
  * written. The sum of squares is accumulated in fp32 (per lane in order, then
  * a fixed butterfly over the wavefront), so rstd is deterministic; y may
  * differ from an exact evaluation by one bf16 unit in the last place.
- * Shape: K % 128 == 0; M any (M % 128 == 0 when the transposed output is
- * asked for). Two kernel launches (the row statistics, then the quantizing
+ * Shape: K % 128 == 0; M any (the transposed outputs are [K, Mp] and
+ * [K, Mp/128], Mp = M rounded up to 128, as transpose_quantize_128x1). Two kernel launches (the row statistics, then the quantizing
  * pass); rstd doubles as the buffer between them.
  */
 int rmsnorm_quantize_1x128(const void* x, const void* gamma, float eps, int64_t M, int64_t K,
@@ -165,8 +169,8 @@ int rmsnorm_quantize_1x128(const void* x, const void* gamma, float eps, int64_t 
  * The codes are those of the bf16 values h, bit for bit, whether or not h is
  * written; h may differ from an exact evaluation by one bf16 unit in the last
  * place.
- * Shape: N % 128 == 0; M any (M % 128 == 0 when the transposed output is
- * asked for).
+ * Shape: N % 128 == 0; M any (the transposed outputs are [N, Mp] and
+ * [N, Mp/128], Mp = M rounded up to 128, as transpose_quantize_128x1).
  */
 int swiglu_quantize_1x128(const void* gate, const void* up, int64_t M, int64_t N, void* h,
                           uint8_t* hq, float* hs, uint8_t* hq_t, float* hs_t, void* stream);
@@ -210,7 +214,9 @@ int fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, co
  *   xq_t  in : E4M3 [K, M], xs_t  in: fp32 [K, M/128]  (transpose_quantize_128x1 of X)
  *   dw    out: bf16 [N, K]
  *   dw[n, k] = bf16( sum_mb dys_t[n,mb] * xs_t[k,mb] * sum_{m in mb} dyq_t[n,m]*xq_t[k,m] )
- * Shape: M % 128 == 0, N % 128 == 0, K % 128 == 0, M < 2^24.
+ * Shape: M % 128 == 0, N % 128 == 0, K % 128 == 0, M < 2^24. For a ragged
+ * token count pass the padded Mp of the 128x1 quantizers' outputs (their
+ * padded codes are +0 and contribute nothing).
  */
 int fp8_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t, const float* xs_t,
                    void* dw, int64_t M, int64_t N, int64_t K, void* stream);

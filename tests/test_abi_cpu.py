@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_strerror(lib):
     lib.fp8bsq_abi_version.restype = ctypes.c_int
-    assert lib.fp8bsq_abi_version() == 3
+    assert lib.fp8bsq_abi_version() == 4
     lib.fp8bsq_strerror.restype = ctypes.c_char_p
     lib.fp8bsq_strerror.argtypes = [ctypes.c_int]
     for code in range(5):
@@ -68,8 +68,9 @@ def test_quantizer_validation(lib):
     assert w(FAKE, 128, 128, FAKE, FAKE, MISALIGNED, None) == 3
     t = lib.transpose_quantize_128x1
     t.argtypes = [P, I64, I64, P, P, P]
-    assert t(FAKE, 64, 128, FAKE, FAKE, None) == 2         # M must be a multiple of 128
-    assert t(FAKE, 128, 64, FAKE, FAKE, None) == 2         # C too
+    assert t(FAKE, 64, 64, FAKE, FAKE, None) == 2          # C grouped by 128 (any M)
+    assert t(FAKE, (1 << 31) - 100, 128, FAKE, FAKE, None) == 2   # M rounded up to 128 is too large
+    assert t(None, 64, 128, FAKE, FAKE, None) == 1         # a ragged M passes the shape check
     assert t(FAKE, 128, 128, FAKE, None, None) == 1
     c = lib.fp8bsq_cast_f32_e4m3
     c.argtypes = [P, P, I64, P]
@@ -81,7 +82,7 @@ def test_dual_quantizer_validation(lib):
     d = lib.quantize_dual_1x128_128x1
     d.argtypes = [P, I64, I64, P, P, P, P, P]
     d.restype = ctypes.c_int
-    assert d(FAKE, 64, 128, FAKE, FAKE, FAKE, FAKE, None) == 2        # tokens grouped by 128
+    assert d(None, 64, 128, FAKE, FAKE, FAKE, FAKE, None) == 1        # a ragged M passes the shape check
     assert d(FAKE, 128, 96, FAKE, FAKE, FAKE, FAKE, None) == 2        # channels grouped by 128
     assert d(FAKE, -128, 128, FAKE, FAKE, FAKE, FAKE, None) == 2
     assert d(FAKE, 128, 128, FAKE, FAKE, None, FAKE, None) == 1       # every output is required
@@ -94,7 +95,7 @@ def test_fused_producer_validation(lib):
     r.argtypes = [P, P, ctypes.c_float, I64, I64, P, P, P, P, P, P, P]
     r.restype = ctypes.c_int
     assert r(FAKE, FAKE, 1e-6, 3, 96, FAKE, None, FAKE, FAKE, None, None, None) == 2    # K % 128
-    assert r(FAKE, FAKE, 1e-6, 3, 128, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 2   # transposed needs M % 128
+    assert r(None, FAKE, 1e-6, 3, 128, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 1   # ragged M with transposed outputs
     assert r(FAKE, FAKE, -1.0, 3, 128, FAKE, None, FAKE, FAKE, None, None, None) == 5   # eps < 0
     assert r(FAKE, FAKE, float("nan"), 3, 128, FAKE, None, FAKE, FAKE, None, None, None) == 5
     assert r(FAKE, FAKE, float("inf"), 3, 128, FAKE, None, FAKE, FAKE, None, None, None) == 5
@@ -106,7 +107,7 @@ def test_fused_producer_validation(lib):
     w.argtypes = [P, P, I64, I64, P, P, P, P, P, P]
     w.restype = ctypes.c_int
     assert w(FAKE, FAKE, 5, 100, None, FAKE, FAKE, None, None, None) == 2
-    assert w(FAKE, FAKE, 5, 128, None, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert w(FAKE, None, 5, 128, None, FAKE, FAKE, FAKE, FAKE, None) == 1     # ragged M with transposed outputs
     assert w(FAKE, None, 5, 128, None, FAKE, FAKE, None, None, None) == 1
     assert w(FAKE, FAKE, 5, 128, MISALIGNED, FAKE, FAKE, None, None, None) == 3
     assert w(None, None, 0, 128, None, None, None, None, None, None) == 0

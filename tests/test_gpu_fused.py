@@ -54,7 +54,7 @@ def _rstd_bound(K):
 
 
 @pytest.mark.parametrize("M,K,transposed", [(3, 384, False), (128, 640, True), (257, 1280, False),
-                                            (256, 5120, True)])
+                                            (256, 5120, True), (300, 640, True)])
 def test_rmsnorm_quantize_matches_oracle(M, K, transposed):
     note(f"rmsnorm_quantize M={M} K={K} transposed={transposed}")
     x = _np_bf16((M, K), seed=M + K, outliers=0.01)
@@ -97,7 +97,8 @@ def test_rmsnorm_edge_rows():
     assert np.all(yb[0] == 0x3F80) and np.all(yb[1] == 0xBF80)
 
 
-@pytest.mark.parametrize("M,N,transposed", [(5, 384, False), (128, 640, True), (256, 27648, True)])
+@pytest.mark.parametrize("M,N,transposed", [(5, 384, False), (128, 640, True), (256, 27648, True),
+                                            (200, 384, True)])
 def test_swiglu_quantize_matches_oracle(M, N, transposed):
     note(f"swiglu_quantize M={M} N={N} transposed={transposed}")
     gt = _np_bf16((M, N), seed=3 * M + N, std=2.0)

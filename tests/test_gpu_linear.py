@@ -93,11 +93,24 @@ def test_weight_update_requantizes():
     assert torch.equal(y1.float(), 2.0 * y0.float())
 
 
-def test_training_rejects_ragged_token_count():
-    lin = _layer(256, 128, seed=60)
-    x = inputs.bf16_normal_device((100, 256), 1.0, 0.0, seed=61)
-    with pytest.raises(ValueError):
-        lin(x)
+def test_training_with_a_ragged_token_count():
+    M, K, N = 300, 256, 384
+    note(f"FP8Linear training with M={M} tokens (transposed copies padded to 384)")
+    lin = _layer(K, N, seed=60)
+    x = inputs.bf16_normal_device((M, K), 1.0, 0.0, seed=61).requires_grad_(True)
+    dy = inputs.bf16_normal_device((M, N), 1e-3, 0.0, seed=62)
+    y = lin(x)
+    y.backward(dy)
     with torch.no_grad():
-        y = lin(x)                                 # inference takes any token count
-    assert y.shape == (100, 128)
+        y_inf = lin(x.detach())
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_inf)
+    xb, wb, db = host_bits(x.detach()), host_bits(lin.weight.detach()), host_bits(dy)
+    oq, os_ = quant.quantize_act_1x128(db)
+    owq, ows, _ = quant.quantize_weight_128x128(wb)
+    ok, info = gemm.within_tolerance(host_bits(x.grad), gemm.gemm_dgrad(oq, os_, owq, ows))
+    assert ok, info
+    o1, s1 = quant.transpose_quantize_128x1(db)          # [N, 384], +0 past token 300
+    o2, s2 = quant.transpose_quantize_128x1(xb)
+    ok, info = gemm.within_tolerance(host_bits(lin.weight.grad), gemm.gemm_wgrad(o1, s1, o2, s2))
+    assert ok, info

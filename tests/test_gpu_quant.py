@@ -150,12 +150,37 @@ def test_transpose_full_size_sampled_and_identity():
     assert torch.equal(qt2, q1) and torch.equal(st2, s1)
 
 
+@pytest.mark.parametrize("M", [1, 100, 300, 1000])
+def test_transpose_ragged_token_count(M):
+    note(f"transpose_128x1 ragged M={M}")
+    x = _np_bf16(M, 384, seed=7 * M)
+    qt, st = fq.transpose_quantize_128x1(dev_bf16(x))
+    torch.cuda.synchronize()
+    oq, os_ = quant.transpose_quantize_128x1(x)
+    assert np.array_equal(host(st), os_)
+    assert np.array_equal(host(qt), oq)
+
+
 # ------------------------------------------------------------ dual output --
 
 @pytest.mark.parametrize("shape", [(128, 128), (256, 384), (384, 640), (512, 1152)])
 def test_dual_matches_oracle(shape):
     note(f"dual 1x128 + 128x1 {shape}")
     x = _np_bf16(*shape, seed=5 * sum(shape))
+    xq, xs, qt, st = fq.quantize_dual_1x128_128x1(dev_bf16(x))
+    torch.cuda.synchronize()
+    oq, os_ = quant.quantize_act_1x128(x)
+    oqt, ost = quant.transpose_quantize_128x1(x)
+    assert_bytes_equal(host(xq), oq, "xq", x)
+    assert_bytes_equal(host(xs), os_, "xs")
+    assert np.array_equal(host(qt), oqt)
+    assert np.array_equal(host(st), ost)
+
+
+@pytest.mark.parametrize("M", [77, 300])
+def test_dual_ragged_token_count(M):
+    note(f"dual ragged M={M}")
+    x = _np_bf16(M, 640, seed=11 * M)
     xq, xs, qt, st = fq.quantize_dual_1x128_128x1(dev_bf16(x))
     torch.cuda.synchronize()
     oq, os_ = quant.quantize_act_1x128(x)
