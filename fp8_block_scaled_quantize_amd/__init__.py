@@ -21,6 +21,9 @@ Entry points (same names as the C ABI):
     fp8_gemm_fwd(xq, xs, wq, ws)      -> y  [M,N] bf16      (Y = X W^T)
     fp8_gemm_dgrad(dyq, dys, wq_t, ws) -> dx [M,K] bf16     (dX = dY W)
     fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t) -> dw [N,K] bf16 (dW = dY^T X)
+    fp8_gemm_{fwd,dgrad,wgrad}_grouped(problems, outs=None)
+                                      -> list of outputs; each problem is the tuple of
+                                         tensors the plain call takes, all in one launch
     cast_f32_e4m3(v)                  -> E4M3 bytes of fp32 values
 E4M3 codes are returned as uint8 tensors (OCP E4M3 bytes); view them as
 ``torch.float8_e4m3fn`` if needed. Every function accepts preallocated
@@ -34,6 +37,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8bsq.so")
 
 _lib = None
+
+
+class GemmProblem(ctypes.Structure):
+    """One problem of a grouped GEMM call (the C ABI's fp8bsq_gemm_problem)."""
+    _fields_ = [("a", ctypes.c_void_p), ("as_", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("bs", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
 class Fp8bsqError(RuntimeError):
@@ -74,6 +84,9 @@ def load_library():
         "fp8_gemm_dgrad": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
         "fp8_gemm_wgrad": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
         "fp8bsq_cast_f32_e4m3": ([vp, vp, i64, vp], i32),
+        "fp8_gemm_fwd_grouped": ([ctypes.POINTER(GemmProblem), i32, vp], i32),
+        "fp8_gemm_dgrad_grouped": ([ctypes.POINTER(GemmProblem), i32, vp], i32),
+        "fp8_gemm_wgrad_grouped": ([ctypes.POINTER(GemmProblem), i32, vp], i32),
     }
     for name, (args, res) in sigs.items():
         f = getattr(lib, name)
@@ -260,6 +273,56 @@ def fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, out=None):
     _check("fp8_gemm_wgrad", load_library().fp8_gemm_wgrad(
         _ptr(dyq_t), _ptr(dys_t), _ptr(xq_t), _ptr(xs_t), _ptr(dw), M, N, K, _stream(dyq_t)))
     return dw
+
+
+def _grouped(role, problems, outs):
+    """Shared marshalling of the grouped GEMMs: validate like the plain calls,
+    allocate outputs, pass one array of problems."""
+    import torch
+    arr = (GemmProblem * max(1, len(problems)))()
+    results = []
+    for g, (a, as_, b, bs) in enumerate(problems):
+        if role == "fwd":
+            M, K = a.shape
+            N = b.shape[0]
+            _need(a, "xq", torch.uint8, (M, K)); _need(as_, "xs", torch.float32, (M, K // 128))
+            _need(b, "wq", torch.uint8, (N, K)); _need(bs, "ws", torch.float32, (N // 128, K // 128))
+            shape = (M, N)
+        elif role == "dgrad":
+            M, N = a.shape
+            K = b.shape[0]
+            _need(a, "dyq", torch.uint8, (M, N)); _need(as_, "dys", torch.float32, (M, N // 128))
+            _need(b, "wq_t", torch.uint8, (K, N)); _need(bs, "ws", torch.float32, (N // 128, K // 128))
+            shape = (M, K)
+        else:
+            N, M = a.shape
+            K = b.shape[0]
+            _need(a, "dyq_t", torch.uint8, (N, M)); _need(as_, "dys_t", torch.float32, (N, M // 128))
+            _need(b, "xq_t", torch.uint8, (K, M)); _need(bs, "xs_t", torch.float32, (K, M // 128))
+            shape = (N, K)
+        out = _out(None if outs is None else outs[g], "out", torch.bfloat16, shape, a)
+        results.append(out)
+        arr[g] = GemmProblem(a.data_ptr(), as_.data_ptr(), b.data_ptr(), bs.data_ptr(), out.data_ptr(), M, N, K)
+    if not problems:
+        return results
+    fn = getattr(load_library(), f"fp8_gemm_{role}_grouped")
+    _check(f"fp8_gemm_{role}_grouped", fn(arr, len(problems), _stream(problems[0][0])))
+    return results
+
+
+def fp8_gemm_fwd_grouped(problems, outs=None):
+    """problems: [(xq, xs, wq, ws), ...] -> [y, ...] in one launch."""
+    return _grouped("fwd", problems, outs)
+
+
+def fp8_gemm_dgrad_grouped(problems, outs=None):
+    """problems: [(dyq, dys, wq_t, ws), ...] -> [dx, ...] in one launch."""
+    return _grouped("dgrad", problems, outs)
+
+
+def fp8_gemm_wgrad_grouped(problems, outs=None):
+    """problems: [(dyq_t, dys_t, xq_t, xs_t), ...] -> [dw, ...] in one launch."""
+    return _grouped("wgrad", problems, outs)
 
 
 def cast_f32_e4m3(v, out=None):

@@ -26,6 +26,28 @@ bool dims_ok(int64_t a, int64_t b) {
 // transposed (128x1) outputs.
 int64_t round128(int64_t m) { return (m + 127) / 128 * 128; }
 
+enum class Role { Fwd, Dgrad, Wgrad };
+constexpr int kLaunch = -1;   // check_problem: valid and not empty
+
+// The checks of one GEMM call (the same for a plain and a grouped call):
+// an error status, FP8BSQ_OK for an empty output (nothing to do), or kLaunch.
+int check_problem(Role role, const fp8bsq_gemm_problem& p) {
+  const int64_t M = p.M, N = p.N, K = p.K;
+  // contraction length and the two output dimensions of each role
+  const int64_t red = role == Role::Fwd ? K : role == Role::Dgrad ? N : M;
+  const int64_t o1 = role == Role::Wgrad ? N : M;
+  const int64_t o2 = role == Role::Fwd ? N : K;
+  if (!dims_ok(M, N) || !dims_ok(M, K) || !dims_ok(N, K) || N % 128 || K % 128 ||
+      (role == Role::Wgrad && M % 128) || red >= kMaxContraction)
+    return FP8BSQ_ERR_SHAPE;
+  if (o1 == 0 || o2 == 0) return FP8BSQ_OK;
+  if (red == 0) return FP8BSQ_ERR_SHAPE;  // an empty contraction would leave the output unwritten
+  if (!p.a || !p.as || !p.b || !p.bs || !p.out) return FP8BSQ_ERR_NULL;
+  if (!aligned16(p.a) || !aligned16(p.as) || !aligned16(p.b) || !aligned16(p.bs) || !aligned16(p.out))
+    return FP8BSQ_ERR_ALIGN;
+  return kLaunch;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? FP8BSQ_OK : FP8BSQ_ERR_HIP; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -114,39 +136,66 @@ int swiglu_quantize_1x128(const void* gate, const void* up, int64_t M, int64_t N
 
 int fp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y,
                  int64_t M, int64_t N, int64_t K, void* stream) {
-  if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N) || N % 128 || K % 128 || K >= kMaxContraction)
-    return FP8BSQ_ERR_SHAPE;
-  if (M == 0 || N == 0) return FP8BSQ_OK;
-  if (K == 0) return FP8BSQ_ERR_SHAPE;  // an empty contraction would leave y unwritten
-  if (!xq || !xs || !wq || !ws || !y) return FP8BSQ_ERR_NULL;
-  if (!aligned16(xq) || !aligned16(xs) || !aligned16(wq) || !aligned16(ws) || !aligned16(y))
-    return FP8BSQ_ERR_ALIGN;
+  const fp8bsq_gemm_problem pr{xq, xs, wq, ws, y, M, N, K};
+  const int st = check_problem(Role::Fwd, pr);
+  if (st != kLaunch) return st;
   return hip_status(fp8bsq::launch_gemm_fwd(xq, xs, wq, ws, y, M, N, K, as_stream(stream)));
 }
 
 int fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
                    void* dx, int64_t M, int64_t N, int64_t K, void* stream) {
-  if (!dims_ok(M, N) || !dims_ok(K, N) || !dims_ok(M, K) || N % 128 || K % 128 || N >= kMaxContraction)
-    return FP8BSQ_ERR_SHAPE;
-  if (M == 0 || K == 0) return FP8BSQ_OK;
-  if (N == 0) return FP8BSQ_ERR_SHAPE;
-  if (!dyq || !dys || !wq_t || !ws || !dx) return FP8BSQ_ERR_NULL;
-  if (!aligned16(dyq) || !aligned16(dys) || !aligned16(wq_t) || !aligned16(ws) || !aligned16(dx))
-    return FP8BSQ_ERR_ALIGN;
+  const fp8bsq_gemm_problem pr{dyq, dys, wq_t, ws, dx, M, N, K};
+  const int st = check_problem(Role::Dgrad, pr);
+  if (st != kLaunch) return st;
   return hip_status(fp8bsq::launch_gemm_dgrad(dyq, dys, wq_t, ws, dx, M, N, K, as_stream(stream)));
 }
 
 int fp8_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t, const float* xs_t,
                    void* dw, int64_t M, int64_t N, int64_t K, void* stream) {
-  if (!dims_ok(N, M) || !dims_ok(K, M) || !dims_ok(N, K) || M % 128 || N % 128 || K % 128 ||
-      M >= kMaxContraction)
-    return FP8BSQ_ERR_SHAPE;
-  if (N == 0 || K == 0) return FP8BSQ_OK;
-  if (M == 0) return FP8BSQ_ERR_SHAPE;
-  if (!dyq_t || !dys_t || !xq_t || !xs_t || !dw) return FP8BSQ_ERR_NULL;
-  if (!aligned16(dyq_t) || !aligned16(dys_t) || !aligned16(xq_t) || !aligned16(xs_t) || !aligned16(dw))
-    return FP8BSQ_ERR_ALIGN;
+  const fp8bsq_gemm_problem pr{dyq_t, dys_t, xq_t, xs_t, dw, M, N, K};
+  const int st = check_problem(Role::Wgrad, pr);
+  if (st != kLaunch) return st;
   return hip_status(fp8bsq::launch_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t, dw, M, N, K, as_stream(stream)));
+}
+
+static int gemm_grouped(Role role, const fp8bsq_gemm_problem* problems, int count, void* stream) {
+  if (count < 0) return FP8BSQ_ERR_SHAPE;
+  if (count == 0) return FP8BSQ_OK;
+  if (!problems) return FP8BSQ_ERR_NULL;
+  int live = 0;
+  for (int g = 0; g < count; ++g) {         // every problem is checked before any launch
+    const int st = check_problem(role, problems[g]);
+    if (st == kLaunch) ++live;
+    else if (st != FP8BSQ_OK) return st;
+  }
+  if (live == 0) return FP8BSQ_OK;
+  fp8bsq::GemmProblem buf[64];
+  const fp8bsq::GemmRole r = role == Role::Fwd ? fp8bsq::GemmRole::Fwd
+                             : role == Role::Dgrad ? fp8bsq::GemmRole::Dgrad : fp8bsq::GemmRole::Wgrad;
+  int n = 0;
+  for (int g = 0; g < count; ++g) {
+    const fp8bsq_gemm_problem& p = problems[g];
+    if (check_problem(role, p) != kLaunch) continue;
+    buf[n++] = fp8bsq::GemmProblem{p.a, p.as, p.b, p.bs, p.out, p.M, p.N, p.K};
+    if (n == 64) {
+      const int st = hip_status(fp8bsq::launch_gemm_grouped(r, buf, n, as_stream(stream)));
+      if (st != FP8BSQ_OK) return st;
+      n = 0;
+    }
+  }
+  return n ? hip_status(fp8bsq::launch_gemm_grouped(r, buf, n, as_stream(stream))) : FP8BSQ_OK;
+}
+
+int fp8_gemm_fwd_grouped(const fp8bsq_gemm_problem* problems, int count, void* stream) {
+  return gemm_grouped(Role::Fwd, problems, count, stream);
+}
+
+int fp8_gemm_dgrad_grouped(const fp8bsq_gemm_problem* problems, int count, void* stream) {
+  return gemm_grouped(Role::Dgrad, problems, count, stream);
+}
+
+int fp8_gemm_wgrad_grouped(const fp8bsq_gemm_problem* problems, int count, void* stream) {
+  return gemm_grouped(Role::Wgrad, problems, count, stream);
 }
 
 int fp8bsq_cast_f32_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {

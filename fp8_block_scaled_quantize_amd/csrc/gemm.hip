@@ -128,8 +128,11 @@ __device__ __forceinline__ void wait_dma_keep() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// One workgroup's output tile: tile number `bid` of the `nblk` tiles of
+// problem p (a plain launch passes its block index and grid size; a grouped
+// launch its block's offset within the problem).
 template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
-__global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmParams p) {
+__device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses LDS address-space casts, device pass only
   using C = GemmCfg<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST>;
   __shared__ __align__(16) uint8_t tiles[NST][C::TILE_BYTES];
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
   const int g = lane >> 4, r16 = lane & 15;
 
   int ti, tj;
-  map_tile(blockIdx.x, gridDim.x, p.tiles_i, p.tiles_j, ti, tj);
+  map_tile(bid, nblk, p.tiles_i, p.tiles_j, ti, tj);
   // The last tile along a dimension is shifted back to end at the edge, so
   // every row it loads exists; where it overlaps its neighbour both compute
   // and store the same values. Only a dimension smaller than one tile (the
@@ -437,6 +440,34 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmPa
 #endif
 }
 
+template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
+__global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmParams p) {
+  gemm_body<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP>(p, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// Several problems of one role in one launch: problem g owns the blocks
+// [start[g], start[g+1]); each problem's range starts at a multiple of the XCD
+// count so that its blocks keep the XCD-aware order of a plain launch (the
+// blocks of the padding exit at once).
+constexpr int kMaxGroup = 16;
+struct GroupedParams {
+  int count;
+  int start[kMaxGroup + 1];
+  GemmParams prob[kMaxGroup];
+};
+
+template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
+__global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_grouped_kernel(GroupedParams gp) {
+  const int bid = (int)blockIdx.x;
+  int g = 0;
+  while (g + 1 < gp.count && bid >= gp.start[g + 1]) ++g;   // uniform over the workgroup
+  const GemmParams& p = gp.prob[g];
+  const int nblk = p.tiles_i * p.tiles_j;
+  const int local = bid - gp.start[g];
+  if (local >= nblk) return;
+  gemm_body<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP>(p, local, nblk);
+}
+
 // ----------------------------------------------------------------------------
 // Launch one tile configuration.
 // ----------------------------------------------------------------------------
@@ -470,34 +501,98 @@ static hipError_t run_gemm(GemmParams p, hipStream_t stream) {
   return run_gemm_cfg<2, 1, 4, 4, PS_ROW, 3, true>(p, stream);
 }
 
+template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
+static hipError_t run_grouped_cfg(const GemmParams* probs, int count, hipStream_t stream) {
+  using C = GemmCfg<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST>;
+  GroupedParams gp{};
+  gp.count = count;
+  int total = 0;
+  for (int g = 0; g < count; ++g) {
+    GemmParams q = probs[g];
+    q.tiles_i = (q.I + C::BI - 1) / C::BI;
+    q.tiles_j = (q.J + C::BJ - 1) / C::BJ;
+    gp.prob[g] = q;
+    gp.start[g] = total;
+    total += (q.tiles_i * q.tiles_j + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+  }
+  gp.start[count] = total;
+  hipLaunchKernelGGL((fp8_gemm_grouped_kernel<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP>), dim3(total),
+                     dim3(C::NT), 0, stream, gp);
+  return hipGetLastError();
+}
+
+// One configuration for the whole group: the large one when every problem
+// qualifies for it and the group fills the chip, else the small one.
+template <bool PS_ROW>
+static hipError_t run_grouped(const GemmParams* probs, int count, hipStream_t stream) {
+  bool large_ok = true, small_ok = true;
+  int64_t large_tiles = 0;
+  for (int g = 0; g < count; ++g) {
+    const GemmParams& q = probs[g];
+    large_ok = large_ok && q.I >= 256 && q.J >= 256;
+    small_ok = small_ok && q.I >= 128 && q.J >= 64;
+    large_tiles += (int64_t)((q.I + 255) / 256) * ((q.J + 255) / 256);
+  }
+  if (large_ok && large_tiles >= 256) return run_grouped_cfg<2, 4, 8, 4, PS_ROW, 2, false>(probs, count, stream);
+  if (small_ok) return run_grouped_cfg<2, 1, 4, 4, PS_ROW, 3, false>(probs, count, stream);
+  return run_grouped_cfg<2, 1, 4, 4, PS_ROW, 3, true>(probs, count, stream);
+}
+
+// Operand roles. All three run D[i][j] = sum_k P[i,k] Q[j,k], written to out[j][i].
+static GemmParams fwd_params(const GemmProblem& pr) {
+  GemmParams p{};
+  p.P = pr.b; p.Ps = pr.bs; p.Q = pr.a; p.Qs = pr.as; p.out = static_cast<uint16_t*>(pr.out);
+  p.I = (int)pr.N; p.J = (int)pr.M; p.K = (int)pr.K; p.Kb = (int)(pr.K / 128);
+  p.ps_ib = (int)(pr.K / 128);  // ws[n/128][kb]
+  p.ps_kb = 1;
+  return p;
+}
+
+static GemmParams dgrad_params(const GemmProblem& pr) {
+  GemmParams p{};
+  p.P = pr.b; p.Ps = pr.bs; p.Q = pr.a; p.Qs = pr.as; p.out = static_cast<uint16_t*>(pr.out);
+  p.I = (int)pr.K; p.J = (int)pr.M; p.K = (int)pr.N; p.Kb = (int)(pr.N / 128);
+  p.ps_ib = 1;                  // ws[nb][k/128]: i = k selects the column block
+  p.ps_kb = (int)(pr.K / 128);  //                 the contraction block nb selects the row
+  return p;
+}
+
+static GemmParams wgrad_params(const GemmProblem& pr) {
+  GemmParams p{};
+  p.P = pr.b; p.Ps = pr.bs; p.Q = pr.a; p.Qs = pr.as; p.out = static_cast<uint16_t*>(pr.out);
+  p.I = (int)pr.K; p.J = (int)pr.N; p.K = (int)pr.M; p.Kb = (int)(pr.M / 128);
+  return p;
+}
+
 hipError_t launch_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                            void* y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  GemmParams p{};
-  p.P = wq; p.Ps = ws; p.Q = xq; p.Qs = xs; p.out = static_cast<uint16_t*>(y);
-  p.I = (int)N; p.J = (int)M; p.K = (int)K; p.Kb = (int)(K / 128);
-  p.ps_ib = (int)(K / 128);  // ws[n/128][kb]
-  p.ps_kb = 1;
-  return run_gemm<false>(p, stream);
+  return run_gemm<false>(fwd_params(GemmProblem{xq, xs, wq, ws, y, M, N, K}), stream);
 }
 
 hipError_t launch_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t,
                              const float* ws, void* dx, int64_t M, int64_t N, int64_t K,
                              hipStream_t stream) {
-  GemmParams p{};
-  p.P = wq_t; p.Ps = ws; p.Q = dyq; p.Qs = dys; p.out = static_cast<uint16_t*>(dx);
-  p.I = (int)K; p.J = (int)M; p.K = (int)N; p.Kb = (int)(N / 128);
-  p.ps_ib = 1;               // ws[nb][k/128]: i = k selects the column block
-  p.ps_kb = (int)(K / 128);  //                 the contraction block nb selects the row
-  return run_gemm<false>(p, stream);
+  return run_gemm<false>(dgrad_params(GemmProblem{dyq, dys, wq_t, ws, dx, M, N, K}), stream);
 }
 
 hipError_t launch_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t,
                              const float* xs_t, void* dw, int64_t M, int64_t N, int64_t K,
                              hipStream_t stream) {
-  GemmParams p{};
-  p.P = xq_t; p.Ps = xs_t; p.Q = dyq_t; p.Qs = dys_t; p.out = static_cast<uint16_t*>(dw);
-  p.I = (int)K; p.J = (int)N; p.K = (int)M; p.Kb = (int)(M / 128);
-  return run_gemm<true>(p, stream);
+  return run_gemm<true>(wgrad_params(GemmProblem{dyq_t, dys_t, xq_t, xs_t, dw, M, N, K}), stream);
+}
+
+hipError_t launch_gemm_grouped(GemmRole role, const GemmProblem* problems, int count, hipStream_t stream) {
+  for (int g0 = 0; g0 < count; g0 += kMaxGroup) {
+    const int n = count - g0 < kMaxGroup ? count - g0 : kMaxGroup;
+    GemmParams ps[kMaxGroup];
+    for (int g = 0; g < n; ++g) {
+      const GemmProblem& pr = problems[g0 + g];
+      ps[g] = role == GemmRole::Fwd ? fwd_params(pr) : role == GemmRole::Dgrad ? dgrad_params(pr) : wgrad_params(pr);
+    }
+    const hipError_t e = role == GemmRole::Wgrad ? run_grouped<true>(ps, n, stream) : run_grouped<false>(ps, n, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace fp8bsq

@@ -22,6 +22,20 @@ hipError_t launch_swiglu_quant(const void* gate, const void* up, int64_t M, int6
                                uint8_t* hq, float* hs, uint8_t* hq_t, float* hs_t, hipStream_t stream);
 hipError_t launch_cast_f32_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 
+// One GEMM problem in the C ABI's terms (see include/fp8bsq.h): a/as the
+// token-major operand and its scales, b/bs the weight-side operand.
+struct GemmProblem {
+  const uint8_t* a;
+  const float* as;
+  const uint8_t* b;
+  const float* bs;
+  void* out;
+  int64_t M, N, K;
+};
+enum class GemmRole { Fwd, Dgrad, Wgrad };
+// Several problems of one role in as few launches as possible (16 per launch).
+hipError_t launch_gemm_grouped(GemmRole role, const GemmProblem* problems, int count, hipStream_t stream);
+
 // GEMM roles. All three run the same NT kernel family: D[i][j] = sum_k P[i,k] Q[j,k]
 // written to out[j][i]; they differ in operands and in how the P scale is indexed.
 hipError_t launch_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define FP8BSQ_ABI_VERSION 4
+#define FP8BSQ_ABI_VERSION 5
 
 /* Status codes. */
 #define FP8BSQ_OK 0
@@ -220,6 +220,37 @@ int fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, co
  */
 int fp8_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uint8_t* xq_t, const float* xs_t,
                    void* dw, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Grouped GEMMs -- several problems of one role in as few launches as the
+ * hardware allows (one launch per 16 problems).
+ * Source: the same passages as the single calls above; grouping is a launch
+ * choice, not part of the method.
+ *
+ * Every problem is the argument list of the plain call, in this order:
+ *   fwd:   a = xq,    as = xs,    b = wq,   bs = ws,   out = y  [M, N]
+ *   dgrad: a = dyq,   as = dys,   b = wq_t, bs = ws,   out = dx [M, K]
+ *   wgrad: a = dyq_t, as = dys_t, b = xq_t, bs = xs_t, out = dw [N, K]
+ * Each problem is validated exactly as the plain call (all of them before any
+ * launch; the first error is returned); problems with an empty output are
+ * skipped. Every output is bit-identical to the plain call's. Outputs of
+ * different problems must not overlap.
+ * For grouped callers (several linears of a layer, the experts of a MoE
+ * layer): one launch lets the tiles of small problems fill the compute units
+ * that a single small problem would leave idle.
+ */
+typedef struct fp8bsq_gemm_problem {
+  const uint8_t* a;
+  const float* as;
+  const uint8_t* b;
+  const float* bs;
+  void* out;
+  int64_t M, N, K;
+} fp8bsq_gemm_problem;
+
+int fp8_gemm_fwd_grouped(const fp8bsq_gemm_problem* problems, int count, void* stream);
+int fp8_gemm_dgrad_grouped(const fp8bsq_gemm_problem* problems, int count, void* stream);
+int fp8_gemm_wgrad_grouped(const fp8bsq_gemm_problem* problems, int count, void* stream);
 
 /*
  * fp8bsq_cast_f32_e4m3 -- the library's E4M3 encoder on its own.

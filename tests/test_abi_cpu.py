@@ -30,7 +30,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"quantize_act_1x128", "quantize_weight_128x128", "transpose_quantize_128x1",
                           "quantize_dual_1x128_128x1", "rmsnorm_quantize_1x128", "swiglu_quantize_1x128",
-                          "fp8_gemm_fwd", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
+                          "fp8_gemm_fwd", "fp8_gemm_fwd_grouped", "fp8_gemm_dgrad_grouped",
+                          "fp8_gemm_wgrad_grouped", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
                           "fp8bsq_strerror", "fp8bsq_abi_version", "fp8bsq_cast_f32_e4m3"}
     for n in names:
         assert hasattr(lib, n), n
@@ -38,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_strerror(lib):
     lib.fp8bsq_abi_version.restype = ctypes.c_int
-    assert lib.fp8bsq_abi_version() == 4
+    assert lib.fp8bsq_abi_version() == 5
     lib.fp8bsq_strerror.restype = ctypes.c_char_p
     lib.fp8bsq_strerror.argtypes = [ctypes.c_int]
     for code in range(5):
@@ -138,6 +139,28 @@ def test_gemm_validation(lib):
     assert lib.fp8_gemm_dgrad(None, FAKE, FAKE, FAKE, FAKE, 1, big, 128, None) == 2
     assert lib.fp8_gemm_wgrad(None, FAKE, FAKE, FAKE, FAKE, big - 128, 128, 128, None) == 1
     assert lib.fp8_gemm_wgrad(None, FAKE, FAKE, FAKE, FAKE, big, 128, 128, None) == 2
+
+
+def test_grouped_gemm_validation(lib):
+    import fp8_block_scaled_quantize_amd as fq
+    lib2 = fq.load_library()
+    arr = (fq.GemmProblem * 3)()
+    good = (0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
+    arr[1] = fq.GemmProblem(*good, 128, 128, 96)            # bad K: the whole call fails
+    arr[2] = fq.GemmProblem(*good, 128, 128, 128)
+    for name, empty in (("fp8_gemm_fwd_grouped", (0, 128, 128)), ("fp8_gemm_dgrad_grouped", (0, 128, 128)),
+                        ("fp8_gemm_wgrad_grouped", (128, 0, 128))):
+        arr[0] = fq.GemmProblem(*good, *empty)              # empty output: skipped
+        f = getattr(lib2, name)
+        assert f(arr, 3, None) == 2, name                   # checked before any launch
+        assert f(arr, 1, None) == 0, name                   # only empty problems: no-op
+        assert f(None, 2, None) == 1, name
+        assert f(arr, -1, None) == 2, name
+        assert f(None, 0, None) == 0, name
+    arr[1] = fq.GemmProblem(0x10000, 0x10000, None, 0x10000, 0x10000, 128, 128, 128)
+    assert lib2.fp8_gemm_wgrad_grouped(arr, 3, None) == 1   # a null operand in the second problem
+    arr[1] = fq.GemmProblem(0x10000, 0x10000, 0x10008, 0x10000, 0x10000, 128, 128, 128)
+    assert lib2.fp8_gemm_fwd_grouped(arr, 2, None) == 3
 
 
 def test_binding_has_no_cpu_fallback():

@@ -192,6 +192,38 @@ def test_exact_large_tiles_wgrad(grid):
                           448.0 ** 2 * (os1.astype(np.float64) @ os2.astype(np.float64).T))
 
 
+# ---------------------------------------------------------- grouped calls --
+
+def _quantized_problem(role, M, N, K, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    u8 = lambda *sh: torch.randint(0, 0x7E, sh, dtype=torch.uint8, device="cuda", generator=g) | (
+        torch.randint(0, 2, sh, dtype=torch.uint8, device="cuda", generator=g) << 7)
+    f32 = lambda *sh: torch.rand(sh, device="cuda", generator=g) * 0.01 + 1e-3
+    if role == "fwd":
+        return (u8(M, K), f32(M, K // 128), u8(N, K), f32(N // 128, K // 128))
+    if role == "dgrad":
+        return (u8(M, N), f32(M, N // 128), u8(K, N), f32(N // 128, K // 128))
+    return (u8(N, M), f32(N, M // 128), u8(K, M), f32(K, M // 128))
+
+
+@pytest.mark.parametrize("role", ["fwd", "dgrad", "wgrad"])
+@pytest.mark.parametrize("shapes", [
+    [(256, 512, 384), (128, 256, 640), (384, 128, 128), (256, 384, 256)],      # small tiles
+    [(256, 4096, 4096), (512, 4224, 2048), (256, 2048, 4096)],                # large tiles
+    [(128, 256, 256)] * 20,                                                   # more than one launch
+])
+def test_grouped_equals_plain_calls(role, shapes):
+    note(f"grouped {role}: {len(shapes)} problems {shapes[:3]}")
+    problems = [_quantized_problem(role, M, N, K, seed=7 * i + len(shapes)) for i, (M, N, K) in enumerate(shapes)]
+    outs = getattr(fq, f"fp8_gemm_{role}_grouped")(problems)
+    plain = getattr(fq, f"fp8_gemm_{role}")
+    refs = [plain(*pr) for pr in problems]
+    torch.cuda.synchronize()
+    for i, (o, r) in enumerate(zip(outs, refs)):
+        assert torch.equal(o, r), f"{role} problem {i}"
+
+
 # ------------------------------------------- oracle operands, small shapes --
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (17, 384, 256), (300, 640, 1152), (64, 256, 4096)])
