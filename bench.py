@@ -4,10 +4,13 @@ One step = the whole hot path for every linear of the workload:
     quantize_weight_128x128(W)            (with the transposed copy for DGrad)
     quantize_dual_1x128_128x1(X)  -> fp8_gemm_fwd      Y  = Xq Wq^T   (+ Xq_t saved for WGrad)
     quantize_dual_1x128_128x1(dY) -> fp8_gemm_dgrad    dX = dYq Wq
-                                  -> fp8_gemm_wgrad    dW = dYq^T Xq
+    fp8_gemm_wgrad_grouped over all linears              dW = dYq^T Xq
 on synthetic inputs already resident in HBM. The dual quantizer emits the
 1x128 and the transposed 128x1 groupings from one read; --separate-quant runs
-quantize_act_1x128 and transpose_quantize_128x1 as separate launches instead. Default workload: the four
+quantize_act_1x128 and transpose_quantize_128x1 as separate launches instead.
+The WGrads of all linears go out as one grouped launch (their tiles fill the
+compute units that the small qkv / o outputs alone leave idle); --no-grouped
+launches them one per linear. Default workload: the four
 linears of a Qwen2.5-32B-shaped layer (qkv 5120->7168, o 5120->5120,
 up 5120->27648, down 27648->5120) at 32768 tokens.
 
@@ -46,6 +49,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-producers", action="store_true",
                     help="skip timing the fused RMSNorm / SwiGLU producers (reported outside the step)")
+    ap.add_argument("--no-grouped", action="store_true",
+                    help="one WGrad launch per linear instead of one grouped launch for all of them")
     ap.add_argument("--separate-quant", action="store_true",
                     help="quantize X and dY with the single-output kernels (two reads each)")
     ap.add_argument("--traffic-from", default=None,
@@ -100,6 +105,7 @@ class Linear:
             self.dyq_t, self.dys_t = e((N, M), u8), e((N, M // 128), f32)
             self.dw = e((N, K), bf)
         self.fq = fq
+        self.defer_wgrad = False
 
     def launches(self):
         """(kind, key, flops, bytes, callable) for every launch of one step, in order.
@@ -139,9 +145,16 @@ class Linear:
             if not dy_dual:
                 L.append(("quant_transpose", f"{self.name}.dy_t[{M},{N}]", 0, act_bytes(M, N),
                           lambda: fq.transpose_quantize_128x1(self.dy, self.dyq_t, self.dys_t)))
-            L.append(("gemm_wgrad", f"{self.name}.wgrad[{N}x{K}x{M}]", 2 * M * N * K, M * N + M * K + 2 * N * K,
-                      lambda: fq.fp8_gemm_wgrad(self.dyq_t, self.dys_t, self.xq_t, self.xs_t, out=self.dw)))
+            if not self.defer_wgrad:
+                L.append(("gemm_wgrad", f"{self.name}.wgrad[{N}x{K}x{M}]", 2 * M * N * K, M * N + M * K + 2 * N * K,
+                          lambda: fq.fp8_gemm_wgrad(self.dyq_t, self.dys_t, self.xq_t, self.xs_t, out=self.dw)))
         return L
+
+    def wgrad_problem(self):
+        """(operands, output, flops, bytes) of this linear's WGrad for a grouped launch."""
+        M, N, K = self.M, self.N, self.K
+        return ((self.dyq_t, self.dys_t, self.xq_t, self.xs_t), self.dw, 2 * M * N * K,
+                M * N + M * K + 2 * N * K)
 
 
 def time_producers(fq, inputs, torch, wl, reps=10):
@@ -303,7 +316,19 @@ def main():
     print(f"[bench] workload {args.workload}: generating inputs", file=sys.stderr, flush=True)
     layers = [Linear(lin, wl["passes"], 1000 + 17 * i, fq, inputs, torch, dual=not args.separate_quant)
               for i, lin in enumerate(wl["linears"])]
+    grouped = not args.no_grouped and "wgrad" in wl["passes"] and len(layers) > 1
+    for layer in layers:
+        layer.defer_wgrad = grouped
     launches = [l for layer in layers for l in layer.launches()]
+    if grouped:
+        # the WGrads of all linears in one launch (they are independent of the
+        # rest of the step; a backward pass can defer them to the end)
+        probs = [layer.wgrad_problem() for layer in layers]
+        outs = [p[1] for p in probs]
+        ops = [p[0] for p in probs]
+        names = "+".join(layer.name for layer in layers)
+        launches.append(("gemm_wgrad", f"wgrad_grouped[{names}]", sum(p[2] for p in probs),
+                         sum(p[3] for p in probs), lambda: fq.fp8_gemm_wgrad_grouped(ops, outs)))
     torch.cuda.synchronize()
     if args.calibrate_copy:
         cx = torch.ones((1 << 29,), dtype=torch.bfloat16, device="cuda")    # 1 GiB
@@ -389,6 +414,7 @@ def main():
         "gemm_ms_per_step": round(gemm_ms, 3),
         "quant_ms_per_step": round(quant_ms, 3),
         "quantizers": "separate" if args.separate_quant else "dual",
+        "wgrad_launch": "grouped" if grouped else "per linear",
         "roofline": roof,
         "kernels": kernels,
     }
