@@ -42,18 +42,27 @@ def dequant_blocks(q, s):
     return decode(q) * np.repeat(np.repeat(s, GROUP, axis=0), GROUP, axis=1)
 
 
-def gemm_fwd(xq, xs, wq, ws):
-    """Forward / rollout: Y[m, n] = sum_k x_hat[m, k] * w_hat[n, k]  (Y = X W^T)."""
-    return dequant_rows(xq, xs) @ dequant_blocks(wq, ws).T
+def gemm_fwd(xq, xs, wq, ws, n=None):
+    """Forward / rollout: Y[m, n] = sum_k x_hat[m, k] * w_hat[n, k]  (Y = X W^T).
+
+    The code tensors may be padded to whole 128-groups (xq [M, Kp], wq [Np, Kp],
+    +0 codes outside the tensor); `n` (default: every row of wq) is the number
+    of output columns N kept.
+    """
+    y = dequant_rows(xq, xs) @ dequant_blocks(wq, ws).T
+    return y if n is None else y[:, :n]
 
 
-def gemm_dgrad(dyq, dys, wq, ws):
+def gemm_dgrad(dyq, dys, wq, ws, k=None):
     """DGrad: dX[m, k] = sum_n dy_hat[m, n] * w_hat[n, k]  (dX = dY W).
 
     Takes the weight in its forward layout wq [N, K]; the contraction runs
     over N, so the 128x128 block scale ws[n/128, k/128] is reused unchanged.
+    With padded code tensors (dyq [M, Np], wq [Np, Kp]) `k` is the number of
+    output columns K kept (default: all).
     """
-    return dequant_rows(dyq, dys) @ dequant_blocks(wq, ws)
+    dx = dequant_rows(dyq, dys) @ dequant_blocks(wq, ws)
+    return dx if k is None else dx[:, :k]
 
 
 def gemm_wgrad(dyq_t, dys_t, xq_t, xs_t):

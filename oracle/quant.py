@@ -18,8 +18,13 @@ binary32, round-to-nearest-even, no flush-to-zero):
                                                then the codec in e4m3.encode)
 
 A group is 128 consecutive elements of a row (1x128), a 128x128 tile
-(128x128), or 128 consecutive rows of one column (128x1). Shapes must be
-multiples of 128 along every grouped dimension.
+(128x128), or 128 consecutive rows of one column (128x1). A dimension that is
+not a multiple of 128 ends in a partial group holding the remaining elements:
+its amax is theirs, and the code tensors are padded to whole groups along that
+dimension with code 0x00 (+0), which a contraction reads as zero products.
+(Reading: the pages fix no layout for a partial group; quantizing the tensor
+zero-padded to whole groups gives exactly these codes and scales, since +0
+never raises an amax and encodes to 0x00.)
 
 Inputs are bf16 bit patterns (uint16 arrays); outputs are E4M3 bytes (uint8)
 and float32 scales.
@@ -63,22 +68,29 @@ def _grouped_scales_and_codes(groups):
     return q, s
 
 
+def _groups(n):
+    """Number of 128-element groups covering n elements, and the padded length."""
+    g = (n + GROUP - 1) // GROUP
+    return g, g * GROUP
+
+
 def quantize_act_1x128(x_bits):
     """1x128 per-token group quantization of a bf16 [M, K] activation.
 
     Source: "Esquema de Cuantización", activations bullet (1x128 per group);
     the same quantizer serves dY before DGrad (backward GEMMs in FP8).
 
-    Returns xq uint8 [M, K] and xs float32 [M, K/128], where xs[m, g] is the
-    scale of x[m, 128g : 128g + 128].
+    Any K is accepted. With Kg = ceil(K / 128) and Kp = 128 * Kg, returns
+    xq uint8 [M, Kp] and xs float32 [M, Kg], where xs[m, g] is the scale of
+    x[m, 128g : min(128g + 128, K)] and xq[m, k] = 0x00 for k >= K.
     """
     x = bf16_bits_to_f32(x_bits)
     M, K = x.shape
-    if K % GROUP:
-        raise ValueError("K must be a multiple of 128")
-    Kg = K // GROUP
-    q, s = _grouped_scales_and_codes(x.reshape(M * Kg, GROUP))
-    return q.reshape(M, K), s.reshape(M, Kg)
+    Kg, Kp = _groups(K)
+    xp = np.zeros((M, Kp), dtype=np.float32)              # +0 beyond the last channel
+    xp[:, :K] = x
+    q, s = _grouped_scales_and_codes(xp.reshape(M * Kg, GROUP))
+    return q.reshape(M, Kp), s.reshape(M, Kg)
 
 
 def quantize_weight_128x128(w_bits):
@@ -87,19 +99,22 @@ def quantize_weight_128x128(w_bits):
     Source: "Esquema de Cuantización", weights bullet (128x128 per block);
     "Arquitectura Central", bf16 master weights re-quantized for each use.
 
-    Returns wq uint8 [N, K], ws float32 [N/128, K/128] (ws[i, j] is the scale
-    of w[128i : 128i + 128, 128j : 128j + 128]) and wq_t = wq transposed
-    ([K, N]), the operand layout DGrad reads. A 128x128 block has the same
-    amax transposed, so wq_t is exactly the byte transpose of wq.
+    Any N and K are accepted. With Nb = ceil(N / 128), Np = 128 * Nb (and Kb,
+    Kp likewise), returns wq uint8 [Np, Kp], ws float32 [Nb, Kb] (ws[i, j] is
+    the scale of the block w[128i : min(128i + 128, N), 128j : min(128j + 128, K)])
+    and wq_t = wq transposed ([Kp, Np]), the operand layout DGrad reads; codes
+    outside [0, N) x [0, K) are 0x00. A 128x128 block has the same amax
+    transposed, so wq_t is exactly the byte transpose of wq.
     """
     w = bf16_bits_to_f32(w_bits)
     N, K = w.shape
-    if N % GROUP or K % GROUP:
-        raise ValueError("N and K must be multiples of 128")
-    Nb, Kb = N // GROUP, K // GROUP
-    blocks = w.reshape(Nb, GROUP, Kb, GROUP).transpose(0, 2, 1, 3)
+    Nb, Np = _groups(N)
+    Kb, Kp = _groups(K)
+    wp = np.zeros((Np, Kp), dtype=np.float32)             # +0 outside the weight
+    wp[:N, :K] = w
+    blocks = wp.reshape(Nb, GROUP, Kb, GROUP).transpose(0, 2, 1, 3)
     q, s = _grouped_scales_and_codes(blocks.reshape(Nb * Kb, GROUP * GROUP))
-    wq = q.reshape(Nb, Kb, GROUP, GROUP).transpose(0, 2, 1, 3).reshape(N, K)
+    wq = q.reshape(Nb, Kb, GROUP, GROUP).transpose(0, 2, 1, 3).reshape(Np, Kp)
     ws = s.reshape(Nb, Kb)
     return wq, ws, np.ascontiguousarray(wq.T)
 
@@ -112,7 +127,8 @@ def transpose_quantize_128x1(x_bits):
     Each group is 128 consecutive tokens of one channel, i.e. it runs along
     the token dimension, which is WGrad's contraction dimension.
 
-    Any token count M is accepted. With Mp = 128 * ceil(M / 128), returns
+    Any token count M and channel count C are accepted (C is not grouped
+    here). With Mp = 128 * ceil(M / 128), returns
     xq_t uint8 [C, Mp] and xs_t float32 [C, Mp/128]: xq_t[c, m] is the code of
     x[m, c] and xs_t[c, b] the scale of the group x[128b : min(128b + 128, M), c].
     When M is not a multiple of 128 the last group holds the remaining tokens
@@ -123,8 +139,7 @@ def transpose_quantize_128x1(x_bits):
     """
     x = bf16_bits_to_f32(x_bits)
     M, C = x.shape
-    Mb = (M + GROUP - 1) // GROUP
-    Mp = Mb * GROUP
+    Mb, Mp = _groups(M)
     xt = np.zeros((C, Mp), dtype=np.float32)            # +0 beyond the last token
     xt[:, :M] = x.T
     q, s = _grouped_scales_and_codes(xt.reshape(C * Mb, GROUP))

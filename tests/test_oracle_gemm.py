@@ -198,3 +198,36 @@ def test_tolerance_boundary():
     assert not ok and info["violations"] == 1
     out = gemm.bf16_rne(np.array([256.0, -1.0, 0.25, 4.0]))  # error 0.25 > 1e-3 * rms
     assert not gemm.within_tolerance(out, ref)[0]
+
+
+def _exact_ragged(rng, rows, cols, e):
+    """bf16 bits of a [rows, cols] tensor whose FP8 quantization is lossless for
+    any rows/cols: values from the small grid times 2^e, and every 1x128 row
+    group (partial ones included) holds a +-448 * 2^e, so every row group and
+    every 128x128 block has scale exactly 2^e."""
+    from fp8_block_scaled_quantize_amd.inputs import SMALL_GRID
+    v = rng.choice(SMALL_GRID, size=(rows, cols)).astype(np.float32)
+    for g in range(-(-cols // 128)):
+        width = min(128, cols - 128 * g)
+        v[np.arange(rows), 128 * g + np.arange(rows) % width] = 448.0
+    v *= rng.choice(np.array([-1.0, 1.0], np.float32), size=(rows, cols))
+    return f32_to_bf16_bits(v * np.float32(2.0 ** e))
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 136, 200), (5, 8, 264), (2, 300, 8)])
+def test_fwd_dgrad_exact_with_partial_groups(M, N, K):
+    """Y = X W^T and dX = dY W through the quantizers for N, K not multiples of
+    128: the padded codes contribute nothing and the kept columns equal the
+    integer product of the (lossless) operands."""
+    rng = np.random.default_rng(M * N + K)
+    x, w, dy = _exact_ragged(rng, M, K, -2), _exact_ragged(rng, N, K, -7), _exact_ragged(rng, M, N, 3)
+    xq, xs = quant.quantize_act_1x128(x)
+    wq, ws, _ = quant.quantize_weight_128x128(w)
+    dyq, dys = quant.quantize_act_1x128(dy)
+    assert np.all(xs == 0.25) and np.all(ws == 2.0 ** -7) and np.all(dys == 8.0)
+    units = lambda bits, sh: np.rint(e4m3.bf16_bits_to_f32(bits).astype(np.float64) * 2.0 ** sh).astype(np.int64)
+    xi, wi, di = units(x, 11), units(w, 16), units(dy, 6)
+    y = gemm.gemm_fwd(xq, xs, wq, ws, n=N)
+    assert y.shape == (M, N) and np.array_equal(y, (xi @ wi.T).astype(np.float64) / 2.0 ** 27)
+    dx = gemm.gemm_dgrad(dyq, dys, wq, ws, k=K)
+    assert dx.shape == (M, K) and np.array_equal(dx, (di @ wi).astype(np.float64) / 2.0 ** 22)

@@ -265,3 +265,71 @@ def test_golden_weight_block():
     wq, ws, wq_t = quant.quantize_weight_128x128(w)
     assert ws[0, 0] == np.float32(scale)
     assert np.array_equal(wq, want) and np.array_equal(wq_t, want.T)
+
+
+# ------------------------------------------------ partial channel groups --
+
+@pytest.mark.parametrize("K", [1, 8, 100, 200, 264])
+def test_act_partial_channel_group(K):
+    # A row length that is not a multiple of 128 ends in a partial group: its
+    # scale and codes are those of the remaining elements alone (exact
+    # rationals + brute-force rounding) and the padded positions hold +0 codes.
+    x = _llama_like(5, K, seed=K)
+    xq, xs = quant.quantize_act_1x128(x)
+    Kg = -(-K // 128)
+    assert xq.shape == (5, 128 * Kg) and xs.shape == (5, Kg)
+    assert np.all(xq[:, K:] == 0)
+    xf = e4m3.bf16_bits_to_f32(x)
+    for m in range(5):
+        for g in range(Kg):
+            vals = xf[m, 128 * g:min(128 * g + 128, K)]
+            sc, codes = _exact_group(vals)
+            assert Fraction(float(xs[m, g])) == sc
+            assert list(xq[m, 128 * g:128 * g + len(vals)]) == codes
+    if K > 128:                       # the whole groups agree with the aligned prefix
+        full = (K // 128) * 128
+        q1, s1 = quant.quantize_act_1x128(np.ascontiguousarray(x[:, :full]))
+        assert np.array_equal(xq[:, :full], q1) and np.array_equal(xs[:, :full // 128], s1)
+
+
+@pytest.mark.parametrize("N,K", [(8, 8), (136, 200), (256, 264), (300, 128)])
+def test_weight_partial_blocks(N, K):
+    # Each block, partial ones included, is quantized over its own elements:
+    # the scale from the exact amax, sampled codes by exact rationals and a
+    # brute-force nearest-code search; everything outside [0,N) x [0,K) is +0.
+    w = _llama_like(N, K, seed=N + 3 * K)
+    wq, ws, wq_t = quant.quantize_weight_128x128(w)
+    Nb, Kb = -(-N // 128), -(-K // 128)
+    assert wq.shape == (128 * Nb, 128 * Kb) and ws.shape == (Nb, Kb) and wq_t.shape == (128 * Kb, 128 * Nb)
+    assert np.all(wq[N:, :] == 0) and np.all(wq[:, K:] == 0)
+    assert np.array_equal(wq_t, wq.T)
+    wf = e4m3.bf16_bits_to_f32(w)
+    rng = np.random.default_rng(N * K)
+    for i in range(Nb):
+        for j in range(Kb):
+            blk = wf[128 * i:min(128 * i + 128, N), 128 * j:min(128 * j + 128, K)]
+            amax = max(abs(Fraction(float(v))) for v in blk.ravel())
+            s = rn_float32(amax / 448)
+            assert Fraction(float(ws[i, j])) == s
+            for _ in range(40):
+                r, c = rng.integers(0, blk.shape[0]), rng.integers(0, blk.shape[1])
+                v = Fraction(float(blk[r, c]))
+                code = nearest_e4m3_code(rn_float32(v / s))
+                if np.signbit(blk[r, c]) and code == 0:
+                    code = 0x80
+                elif v < 0:
+                    code |= 0x80
+                assert wq[128 * i + r, 128 * j + c] == code
+    # a block has the same amax transposed, partial blocks included
+    wq2, ws2, wq2_t = quant.quantize_weight_128x128(np.ascontiguousarray(w.T))
+    assert np.array_equal(wq2, wq.T) and np.array_equal(ws2, ws.T) and np.array_equal(wq2_t, wq)
+
+
+def test_transpose_identity_with_partial_channel_block():
+    # 128x1 groups run along the tokens; a channel count that is not a
+    # multiple of 128 changes nothing for them
+    x = _llama_like(256, 200, seed=13)
+    q1, s1 = quant.quantize_act_1x128(np.ascontiguousarray(x.T))
+    qt, st = quant.transpose_quantize_128x1(x)
+    assert qt.shape == (200, 256)
+    assert np.array_equal(q1, qt) and np.array_equal(s1, st)
