@@ -8,22 +8,24 @@ pointers plus the current HIP stream to the library. Every step of the
 computation runs in the library's HIP kernels; there is no fallback. If the
 library is missing, every call raises.
 
-Entry points (same names as the C ABI):
-    quantize_act_1x128(x)             -> (xq [M,K] uint8, xs [M,K/128] float32)
+Entry points (same names as the C ABI; Kp, Np, Mp are K, N, M rounded up to
+a multiple of 128, Kg = Kp/128; channel counts are any multiple of 8):
+    quantize_act_1x128(x)             -> (xq [M,Kp] uint8, xs [M,Kg] float32)
     quantize_weight_128x128(w, transposed=True)
-                                      -> (wq [N,K], ws [N/128,K/128], wq_t [K,N] or None)
-    transpose_quantize_128x1(x)       -> (xq_t [C,Mp], xs_t [C,Mp/128]), Mp = M rounded up to 128
+                                      -> (wq [Np,Kp], ws [Ng,Kg], wq_t [Kp,Np] or None)
+    transpose_quantize_128x1(x)       -> (xq_t [C,Mp], xs_t [C,Mp/128])
     quantize_dual_1x128_128x1(x)      -> (xq, xs, xq_t, xs_t): both of the above, one read of x
     rmsnorm_quantize_1x128(x, gamma, eps, transposed=False, write_y=False)
                                       -> (xq, xs, xq_t, xs_t, rstd, y): RMSNorm, its output quantized
     swiglu_quantize_1x128(gate, up, transposed=False, write_h=False)
                                       -> (hq, hs, hq_t, hs_t, h): silu(gate)*up, quantized
-    fp8_gemm_fwd(xq, xs, wq, ws)      -> y  [M,N] bf16      (Y = X W^T)
-    fp8_gemm_dgrad(dyq, dys, wq_t, ws) -> dx [M,K] bf16     (dX = dY W)
-    fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t) -> dw [N,K] bf16 (dW = dY^T X)
+    fp8_gemm_fwd(xq, xs, wq, ws, n=None)      -> y  [M,N] bf16   (Y = X W^T; N defaults to Np)
+    fp8_gemm_dgrad(dyq, dys, wq_t, ws, k=None) -> dx [M,K] bf16  (dX = dY W; K defaults to Kp)
+    fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t)  -> dw [N,K] bf16   (dW = dY^T X)
     fp8_gemm_{fwd,dgrad,wgrad}_grouped(problems, outs=None)
                                       -> list of outputs; each problem is the tuple of
-                                         tensors the plain call takes, all in one launch
+                                         tensors the plain call takes (fwd / dgrad: plus,
+                                         optionally, n / k), all in one launch
     cast_f32_e4m3(v)                  -> E4M3 bytes of fp32 values
 E4M3 codes are returned as uint8 tensors (OCP E4M3 bytes); view them as
 ``torch.float8_e4m3fn`` if needed. Every function accepts preallocated
@@ -136,12 +138,19 @@ def _out(t, name, dtype, shape, like):
     return _need(t, name, dtype, shape)
 
 
+def padded(n):
+    """A length rounded up to whole 128-element groups: the grouped dimension of
+    the code tensors (and the token length of the 128x1 outputs)."""
+    return (n + 127) // 128 * 128
+
+
 def quantize_act_1x128(x, xq=None, xs=None):
     import torch
     M, K = x.shape
+    Kp = padded(K)
     _need(x, "x", torch.bfloat16, (M, K))
-    xq = _out(xq, "xq", torch.uint8, (M, K), x)
-    xs = _out(xs, "xs", torch.float32, (M, K // 128), x)
+    xq = _out(xq, "xq", torch.uint8, (M, Kp), x)
+    xs = _out(xs, "xs", torch.float32, (M, Kp // 128), x)
     _check("quantize_act_1x128", load_library().quantize_act_1x128(
         _ptr(x), M, K, _ptr(xq), _ptr(xs), _stream(x)))
     return xq, xs
@@ -150,11 +159,12 @@ def quantize_act_1x128(x, xq=None, xs=None):
 def quantize_weight_128x128(w, transposed=True, wq=None, ws=None, wq_t=None):
     import torch
     N, K = w.shape
+    Np, Kp = padded(N), padded(K)
     _need(w, "w", torch.bfloat16, (N, K))
-    wq = _out(wq, "wq", torch.uint8, (N, K), w)
-    ws = _out(ws, "ws", torch.float32, (N // 128, K // 128), w)
+    wq = _out(wq, "wq", torch.uint8, (Np, Kp), w)
+    ws = _out(ws, "ws", torch.float32, (Np // 128, Kp // 128), w)
     if transposed:
-        wq_t = _out(wq_t, "wq_t", torch.uint8, (K, N), w)
+        wq_t = _out(wq_t, "wq_t", torch.uint8, (Kp, Np), w)
     else:
         wq_t = None
     _check("quantize_weight_128x128", load_library().quantize_weight_128x128(
@@ -164,7 +174,7 @@ def quantize_weight_128x128(w, transposed=True, wq=None, ws=None, wq_t=None):
 
 def padded_tokens(M):
     """Token length of the 128x1 (transposed) outputs: M rounded up to 128."""
-    return (M + 127) // 128 * 128
+    return padded(M)
 
 
 def transpose_quantize_128x1(x, xq_t=None, xs_t=None):
@@ -182,9 +192,10 @@ def transpose_quantize_128x1(x, xq_t=None, xs_t=None):
 def quantize_dual_1x128_128x1(x, xq=None, xs=None, xq_t=None, xs_t=None):
     import torch
     M, K = x.shape
+    Kp = padded(K)
     _need(x, "x", torch.bfloat16, (M, K))
-    xq = _out(xq, "xq", torch.uint8, (M, K), x)
-    xs = _out(xs, "xs", torch.float32, (M, K // 128), x)
+    xq = _out(xq, "xq", torch.uint8, (M, Kp), x)
+    xs = _out(xs, "xs", torch.float32, (M, Kp // 128), x)
     Mp = padded_tokens(M)
     xq_t = _out(xq_t, "xq_t", torch.uint8, (K, Mp), x)
     xs_t = _out(xs_t, "xs_t", torch.float32, (K, Mp // 128), x)
@@ -199,8 +210,8 @@ def rmsnorm_quantize_1x128(x, gamma, eps=1e-6, transposed=False, write_y=False,
     M, K = x.shape
     _need(x, "x", torch.bfloat16, (M, K))
     _need(gamma, "gamma", torch.bfloat16, (K,))
-    xq = _out(xq, "xq", torch.uint8, (M, K), x)
-    xs = _out(xs, "xs", torch.float32, (M, K // 128), x)
+    xq = _out(xq, "xq", torch.uint8, (M, padded(K)), x)
+    xs = _out(xs, "xs", torch.float32, (M, padded(K) // 128), x)
     rstd = _out(rstd, "rstd", torch.float32, (M,), x)
     if transposed:
         xq_t = _out(xq_t, "xq_t", torch.uint8, (K, padded_tokens(M)), x)
@@ -220,8 +231,8 @@ def swiglu_quantize_1x128(gate, up, transposed=False, write_h=False,
     M, N = gate.shape
     _need(gate, "gate", torch.bfloat16, (M, N))
     _need(up, "up", torch.bfloat16, (M, N))
-    hq = _out(hq, "hq", torch.uint8, (M, N), gate)
-    hs = _out(hs, "hs", torch.float32, (M, N // 128), gate)
+    hq = _out(hq, "hq", torch.uint8, (M, padded(N)), gate)
+    hs = _out(hs, "hs", torch.float32, (M, padded(N) // 128), gate)
     if transposed:
         hq_t = _out(hq_t, "hq_t", torch.uint8, (N, padded_tokens(M)), gate)
         hs_t = _out(hs_t, "hs_t", torch.float32, (N, padded_tokens(M) // 128), gate)
@@ -233,31 +244,43 @@ def swiglu_quantize_1x128(gate, up, transposed=False, write_h=False,
     return hq, hs, hq_t, hs_t, h
 
 
-def fp8_gemm_fwd(xq, xs, wq, ws, out=None):
+def _cols(n, npad, name):
+    """Logical column count of a GEMM output whose code tensors are padded to npad."""
+    n = npad if n is None else int(n)
+    if padded(n) != npad:
+        raise ValueError(f"{name}={n} does not round up to the padded length {npad} of the codes")
+    return n
+
+
+def fp8_gemm_fwd(xq, xs, wq, ws, out=None, n=None):
+    """Y [M, N] = Xq Wq^T; n is the weight's logical row count N (default: wq's rows)."""
     import torch
-    M, K = xq.shape
-    N = wq.shape[0]
-    _need(xq, "xq", torch.uint8, (M, K))
-    _need(xs, "xs", torch.float32, (M, K // 128))
-    _need(wq, "wq", torch.uint8, (N, K))
-    _need(ws, "ws", torch.float32, (N // 128, K // 128))
+    M, Kp = xq.shape
+    Np = wq.shape[0]
+    N = _cols(n, Np, "n")
+    _need(xq, "xq", torch.uint8, (M, Kp))
+    _need(xs, "xs", torch.float32, (M, Kp // 128))
+    _need(wq, "wq", torch.uint8, (Np, Kp))
+    _need(ws, "ws", torch.float32, (Np // 128, Kp // 128))
     y = _out(out, "out", torch.bfloat16, (M, N), xq)
     _check("fp8_gemm_fwd", load_library().fp8_gemm_fwd(
-        _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y), M, N, K, _stream(xq)))
+        _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y), M, N, Kp, _stream(xq)))
     return y
 
 
-def fp8_gemm_dgrad(dyq, dys, wq_t, ws, out=None):
+def fp8_gemm_dgrad(dyq, dys, wq_t, ws, out=None, k=None):
+    """dX [M, K] = dYq Wq; k is the weight's logical column count K (default: wq_t's rows)."""
     import torch
-    M, N = dyq.shape
-    K = wq_t.shape[0]
-    _need(dyq, "dyq", torch.uint8, (M, N))
-    _need(dys, "dys", torch.float32, (M, N // 128))
-    _need(wq_t, "wq_t", torch.uint8, (K, N))
-    _need(ws, "ws", torch.float32, (N // 128, K // 128))
+    M, Np = dyq.shape
+    Kp = wq_t.shape[0]
+    K = _cols(k, Kp, "k")
+    _need(dyq, "dyq", torch.uint8, (M, Np))
+    _need(dys, "dys", torch.float32, (M, Np // 128))
+    _need(wq_t, "wq_t", torch.uint8, (Kp, Np))
+    _need(ws, "ws", torch.float32, (Np // 128, Kp // 128))
     dx = _out(out, "out", torch.bfloat16, (M, K), dyq)
     _check("fp8_gemm_dgrad", load_library().fp8_gemm_dgrad(
-        _ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws), _ptr(dx), M, N, K, _stream(dyq)))
+        _ptr(dyq), _ptr(dys), _ptr(wq_t), _ptr(ws), _ptr(dx), M, Np, K, _stream(dyq)))
     return dx
 
 
@@ -281,18 +304,22 @@ def _grouped(role, problems, outs):
     import torch
     arr = (GemmProblem * max(1, len(problems)))()
     results = []
-    for g, (a, as_, b, bs) in enumerate(problems):
+    for g, prob in enumerate(problems):
+        a, as_, b, bs = prob[:4]
+        cols = prob[4] if len(prob) > 4 else None
         if role == "fwd":
             M, K = a.shape
-            N = b.shape[0]
+            Np = b.shape[0]
+            N = _cols(cols, Np, "n")
             _need(a, "xq", torch.uint8, (M, K)); _need(as_, "xs", torch.float32, (M, K // 128))
-            _need(b, "wq", torch.uint8, (N, K)); _need(bs, "ws", torch.float32, (N // 128, K // 128))
+            _need(b, "wq", torch.uint8, (Np, K)); _need(bs, "ws", torch.float32, (Np // 128, K // 128))
             shape = (M, N)
         elif role == "dgrad":
             M, N = a.shape
-            K = b.shape[0]
+            Kp = b.shape[0]
+            K = _cols(cols, Kp, "k")
             _need(a, "dyq", torch.uint8, (M, N)); _need(as_, "dys", torch.float32, (M, N // 128))
-            _need(b, "wq_t", torch.uint8, (K, N)); _need(bs, "ws", torch.float32, (N // 128, K // 128))
+            _need(b, "wq_t", torch.uint8, (Kp, N)); _need(bs, "ws", torch.float32, (N // 128, Kp // 128))
             shape = (M, K)
         else:
             N, M = a.shape

@@ -22,9 +22,12 @@ bool dims_ok(int64_t a, int64_t b) {
   return a == 0 || b < kMaxElems / a;
 }
 
-// Token count rounded up to a whole 128-token block: the token length of the
-// transposed (128x1) outputs.
+// A length rounded up to whole 128-element groups: the token length of the
+// transposed (128x1) outputs and the padded channel length of the code tensors.
 int64_t round128(int64_t m) { return (m + 127) / 128 * 128; }
+
+// Channel dimensions: any multiple of 8 (bf16 rows stay 16-byte aligned).
+bool channels_ok(int64_t c) { return c % 8 == 0; }
 
 enum class Role { Fwd, Dgrad, Wgrad };
 constexpr int kLaunch = -1;   // check_problem: valid and not empty
@@ -34,11 +37,13 @@ constexpr int kLaunch = -1;   // check_problem: valid and not empty
 int check_problem(Role role, const fp8bsq_gemm_problem& p) {
   const int64_t M = p.M, N = p.N, K = p.K;
   // contraction length and the two output dimensions of each role
-  const int64_t red = role == Role::Fwd ? K : role == Role::Dgrad ? N : M;
+  const int64_t Np = round128(N), Kp = round128(K);
+  const int64_t red = role == Role::Fwd ? Kp : role == Role::Dgrad ? Np : M;
   const int64_t o1 = role == Role::Wgrad ? N : M;
   const int64_t o2 = role == Role::Fwd ? N : K;
-  if (!dims_ok(M, N) || !dims_ok(M, K) || !dims_ok(N, K) || N % 128 || K % 128 ||
-      (role == Role::Wgrad && M % 128) || red >= kMaxContraction)
+  if (!dims_ok(M, N) || !dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, Np) || !dims_ok(M, Kp) ||
+      !dims_ok(Np, Kp) || !channels_ok(N) || !channels_ok(K) || (role == Role::Wgrad && M % 128) ||
+      red >= kMaxContraction)
     return FP8BSQ_ERR_SHAPE;
   if (o1 == 0 || o2 == 0) return FP8BSQ_OK;
   if (red == 0) return FP8BSQ_ERR_SHAPE;  // an empty contraction would leave the output unwritten
@@ -60,7 +65,7 @@ const char* fp8bsq_strerror(int status) {
   switch (status) {
     case FP8BSQ_OK: return "ok";
     case FP8BSQ_ERR_NULL: return "a required pointer is NULL";
-    case FP8BSQ_ERR_SHAPE: return "unsupported shape (negative, too large, or not a multiple of 128 where required)";
+    case FP8BSQ_ERR_SHAPE: return "unsupported shape (negative, too large, or not a multiple of 8 / 128 where required)";
     case FP8BSQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case FP8BSQ_ERR_HIP: return "the HIP runtime reported an error at launch";
     case FP8BSQ_ERR_VALUE: return "a scalar argument is out of range";
@@ -71,7 +76,7 @@ const char* fp8bsq_strerror(int status) {
 int fp8bsq_abi_version(void) { return FP8BSQ_ABI_VERSION; }
 
 int quantize_act_1x128(const void* x, int64_t M, int64_t K, uint8_t* xq, float* xs, void* stream) {
-  if (!dims_ok(M, K) || K % 128) return FP8BSQ_ERR_SHAPE;
+  if (!dims_ok(M, K) || !dims_ok(M, round128(K)) || !channels_ok(K)) return FP8BSQ_ERR_SHAPE;
   if (M == 0 || K == 0) return FP8BSQ_OK;
   if (!x || !xq || !xs) return FP8BSQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(xq) || !aligned16(xs)) return FP8BSQ_ERR_ALIGN;
@@ -80,7 +85,8 @@ int quantize_act_1x128(const void* x, int64_t M, int64_t K, uint8_t* xq, float* 
 
 int quantize_weight_128x128(const void* w, int64_t N, int64_t K, uint8_t* wq, float* ws,
                             uint8_t* wq_t, void* stream) {
-  if (!dims_ok(N, K) || N % 128 || K % 128) return FP8BSQ_ERR_SHAPE;
+  if (!dims_ok(N, K) || !dims_ok(round128(N), round128(K)) || !channels_ok(N) || !channels_ok(K))
+    return FP8BSQ_ERR_SHAPE;
   if (N == 0 || K == 0) return FP8BSQ_OK;
   if (!w || !wq || !ws) return FP8BSQ_ERR_NULL;
   if (!aligned16(w) || !aligned16(wq) || !aligned16(ws) || (wq_t && !aligned16(wq_t)))
@@ -90,7 +96,7 @@ int quantize_weight_128x128(const void* w, int64_t N, int64_t K, uint8_t* wq, fl
 
 int transpose_quantize_128x1(const void* x, int64_t M, int64_t C, uint8_t* xq_t, float* xs_t,
                              void* stream) {
-  if (!dims_ok(M, C) || !dims_ok(round128(M), C) || C % 128) return FP8BSQ_ERR_SHAPE;
+  if (!dims_ok(M, C) || !dims_ok(round128(M), C) || !channels_ok(C)) return FP8BSQ_ERR_SHAPE;
   if (M == 0 || C == 0) return FP8BSQ_OK;
   if (!x || !xq_t || !xs_t) return FP8BSQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(xq_t) || !aligned16(xs_t)) return FP8BSQ_ERR_ALIGN;
@@ -99,7 +105,8 @@ int transpose_quantize_128x1(const void* x, int64_t M, int64_t C, uint8_t* xq_t,
 
 int quantize_dual_1x128_128x1(const void* x, int64_t M, int64_t K, uint8_t* xq, float* xs,
                               uint8_t* xq_t, float* xs_t, void* stream) {
-  if (!dims_ok(M, K) || !dims_ok(round128(M), K) || K % 128) return FP8BSQ_ERR_SHAPE;
+  if (!dims_ok(M, K) || !dims_ok(round128(M), K) || !dims_ok(M, round128(K)) || !channels_ok(K))
+    return FP8BSQ_ERR_SHAPE;
   if (M == 0 || K == 0) return FP8BSQ_OK;
   if (!x || !xq || !xs || !xq_t || !xs_t) return FP8BSQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(xq) || !aligned16(xs) || !aligned16(xq_t) || !aligned16(xs_t))
@@ -111,7 +118,8 @@ int rmsnorm_quantize_1x128(const void* x, const void* gamma, float eps, int64_t 
                            float* rstd, void* y, uint8_t* xq, float* xs, uint8_t* xq_t, float* xs_t,
                            void* stream) {
   const bool tr = xq_t != nullptr || xs_t != nullptr;
-  if (!dims_ok(M, K) || !dims_ok(round128(M), K) || K % 128) return FP8BSQ_ERR_SHAPE;
+  if (!dims_ok(M, K) || !dims_ok(round128(M), K) || !dims_ok(M, round128(K)) || !channels_ok(K))
+    return FP8BSQ_ERR_SHAPE;
   if (!(eps >= 0.0f) || eps == INFINITY) return FP8BSQ_ERR_VALUE;
   if (M == 0 || K == 0) return FP8BSQ_OK;
   if (!x || !gamma || !rstd || !xq || !xs || (tr && (!xq_t || !xs_t))) return FP8BSQ_ERR_NULL;
@@ -125,7 +133,8 @@ int rmsnorm_quantize_1x128(const void* x, const void* gamma, float eps, int64_t 
 int swiglu_quantize_1x128(const void* gate, const void* up, int64_t M, int64_t N, void* h,
                           uint8_t* hq, float* hs, uint8_t* hq_t, float* hs_t, void* stream) {
   const bool tr = hq_t != nullptr || hs_t != nullptr;
-  if (!dims_ok(M, N) || !dims_ok(round128(M), N) || N % 128) return FP8BSQ_ERR_SHAPE;
+  if (!dims_ok(M, N) || !dims_ok(round128(M), N) || !dims_ok(M, round128(N)) || !channels_ok(N))
+    return FP8BSQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BSQ_OK;
   if (!gate || !up || !hq || !hs || (tr && (!hq_t || !hs_t))) return FP8BSQ_ERR_NULL;
   if (!aligned16(gate) || !aligned16(up) || !aligned16(hq) || !aligned16(hs) || (h && !aligned16(h)) ||

@@ -9,10 +9,14 @@
 // and Q [J, K] (both K-contiguous E4M3) with one fp32 scale per 128-long
 // K block,
 //     out[j][i] = bf16( sum_kb  ps(i, kb) * qs(j, kb) * sum_{k in kb} P[i,k] * Q[j,k] )
-// and writes out as a row-major [J, I] bf16 matrix.
-//   forward: P = Wq [N, K] (block scales), Q = Xq [M, K]   -> out = Y  [M, N]
-//   DGrad  : P = Wq^T [K, N] (block scales, read transposed), Q = dYq [M, N] -> dX [M, K]
-//   WGrad  : P = Xq^T [K, M] (row scales), Q = dYq^T [N, M] -> dW [N, K]
+// and writes the columns i < Iout of out as a row-major [J, Iout] bf16 matrix.
+//   forward: P = Wq [Np, Kp] (block scales), Q = Xq [M, Kp]   -> out = Y  [M, N]
+//   DGrad  : P = Wq^T [Kp, Np] (block scales, read transposed), Q = dYq [M, Np] -> dX [M, K]
+//   WGrad  : P = Xq^T [K, Mp] (row scales), Q = dYq^T [N, Mp] -> dW [N, K]
+// (Np, Kp, Mp: N, K, M rounded up to 128; the code tensors are padded with +0
+// codes along their grouped dimensions, so the contraction always runs over
+// whole 128-long blocks and the block-scaled P always has whole 128-row
+// blocks; a partial last block of N or K only masks the stored columns.)
 //
 // Each 128-long K block is exactly one v_mfma_f32_16x16x128_f8f6f4 per 16x16
 // output tile, so the block's partial sum comes out of a single MFMA with a
@@ -42,6 +46,7 @@ struct GemmParams {
   const float* Qs;
   uint16_t* out;
   int I, J, K, Kb;
+  int Iout, ldo;     // columns i < Iout of out are stored, rows ldo elements apart
   int ps_ib, ps_kb;  // block P scale of (i, kb) at Ps[(i / 128) * ps_ib + kb * ps_kb]
   int tiles_i, tiles_j;
 };
@@ -433,8 +438,9 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
       const int jr = lane / CHUNKS + ROWS_PER_PASS * k;
       const u32x4 v = *reinterpret_cast<const u32x4*>(eb + jr * ROWB + ((c ^ (jr & (CHUNKS - 1))) * 16));
       const int j = j0 + wj * C::WJ + jr;
-      if (!CLAMP || (j < p.J && i < p.I))
-        *reinterpret_cast<u32x4*>(p.out + (int64_t)j * p.I + i) = v;
+      // Iout is a multiple of 8, so each 16-byte chunk is stored whole or not at all
+      if ((!CLAMP || j < p.J) && i < p.Iout)
+        *reinterpret_cast<u32x4*>(p.out + (int64_t)j * p.ldo + i) = v;
     }
   }
 #endif
@@ -539,21 +545,29 @@ static hipError_t run_grouped(const GemmParams* probs, int count, hipStream_t st
 }
 
 // Operand roles. All three run D[i][j] = sum_k P[i,k] Q[j,k], written to out[j][i].
+// M, N, K are the logical sizes; the code tensors have them rounded up to 128
+// along their grouped dimensions.
+static int blocks128(int64_t n) { return (int)((n + 127) / 128); }
+
 static GemmParams fwd_params(const GemmProblem& pr) {
   GemmParams p{};
+  const int Nb = blocks128(pr.N), Kb = blocks128(pr.K);
   p.P = pr.b; p.Ps = pr.bs; p.Q = pr.a; p.Qs = pr.as; p.out = static_cast<uint16_t*>(pr.out);
-  p.I = (int)pr.N; p.J = (int)pr.M; p.K = (int)pr.K; p.Kb = (int)(pr.K / 128);
-  p.ps_ib = (int)(pr.K / 128);  // ws[n/128][kb]
+  p.I = 128 * Nb; p.J = (int)pr.M; p.K = 128 * Kb; p.Kb = Kb;
+  p.Iout = (int)pr.N; p.ldo = (int)pr.N;
+  p.ps_ib = Kb;  // ws[n/128][kb]
   p.ps_kb = 1;
   return p;
 }
 
 static GemmParams dgrad_params(const GemmProblem& pr) {
   GemmParams p{};
+  const int Nb = blocks128(pr.N), Kb = blocks128(pr.K);
   p.P = pr.b; p.Ps = pr.bs; p.Q = pr.a; p.Qs = pr.as; p.out = static_cast<uint16_t*>(pr.out);
-  p.I = (int)pr.K; p.J = (int)pr.M; p.K = (int)pr.N; p.Kb = (int)(pr.N / 128);
-  p.ps_ib = 1;                  // ws[nb][k/128]: i = k selects the column block
-  p.ps_kb = (int)(pr.K / 128);  //                 the contraction block nb selects the row
+  p.I = 128 * Kb; p.J = (int)pr.M; p.K = 128 * Nb; p.Kb = Nb;
+  p.Iout = (int)pr.K; p.ldo = (int)pr.K;
+  p.ps_ib = 1;   // ws[nb][k/128]: i = k selects the column block
+  p.ps_kb = Kb;  //                 the contraction block nb selects the row
   return p;
 }
 
@@ -561,6 +575,7 @@ static GemmParams wgrad_params(const GemmProblem& pr) {
   GemmParams p{};
   p.P = pr.b; p.Ps = pr.bs; p.Q = pr.a; p.Qs = pr.as; p.out = static_cast<uint16_t*>(pr.out);
   p.I = (int)pr.K; p.J = (int)pr.N; p.K = (int)pr.M; p.Kb = (int)(pr.M / 128);
+  p.Iout = (int)pr.K; p.ldo = (int)pr.K;
   return p;
 }
 

@@ -9,6 +9,14 @@
 // amax is reduced inside the wavefront with DPP moves; the 128x1 kernel
 // transposes its output tile through LDS so both its reads and its writes
 // stay coalesced.
+//
+// Channel counts that are not a multiple of 128 (any multiple of 8, so bf16
+// rows stay 16-byte aligned) end in a partial group. The TAIL instantiation
+// of each kernel reads the 16-byte chunks past the last channel as +0 (from a
+// clamped, in-bounds address): +0 leaves the amax of the valid elements
+// alone and encodes to 0x00, so the code tensors come out padded to whole
+// groups with +0 codes (row length Kp = K rounded up to 128). Aligned shapes
+// run the instantiation without the masks.
 #include "device_common.h"
 #include "launch.h"
 
@@ -21,10 +29,12 @@ constexpr int64_t kMaxGridY = 65535;
 constexpr int64_t kMaxBlocks1D = (int64_t)1 << 22;
 
 // ============================================================================
-// 1x128: a [M, K] tensor with K % 128 == 0 is a flat array of G = M*K/128
-// groups of 128 contiguous elements, and group g's scale is xs[g]. Each group
-// is handled by 8 lanes; lane j holds elements 8j..8j+7 and 64+8j..64+8j+7,
-// so each load instruction reads 128 contiguous bytes per group.
+// 1x128: the codes xq [M, Kp] are a flat array of G = M*Kp/128 groups of 128
+// bytes and group g's scale is xs[g]. With K % 128 == 0 the input is the same
+// flat array of groups; otherwise (TAIL) group g is row g / Kg, group g % Kg
+// of the input. Each group is handled by 8 lanes; lane j holds elements
+// 8j..8j+7 and 64+8j..64+8j+7, so each load instruction reads 128 contiguous
+// bytes per group.
 // ============================================================================
 constexpr int ACT_THREADS = 256;
 constexpr int ACT_PASSES = 2;
@@ -38,9 +48,10 @@ __device__ __forceinline__ void unpack8(const u32x4& r, float* v) {
   v[6] = bf16_lo(r[3]); v[7] = bf16_hi(r[3]);
 }
 
+template <bool TAIL>
 __global__ __launch_bounds__(ACT_THREADS) void quant_act_1x128_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, float* __restrict__ xs, int64_t G,
-    int64_t blk0) {
+    int64_t blk0, int K, int Kg) {
   const int t = threadIdx.x;
   const int j = t & 7;
   const int64_t blk = blk0 + blockIdx.x;
@@ -51,9 +62,19 @@ __global__ __launch_bounds__(ACT_THREADS) void quant_act_1x128_kernel(
     const int64_t g = blk * ACT_GROUPS_PER_BLOCK + p * ACT_GROUPS_PER_PASS + (t >> 3);
     grp[p] = g;
     const int64_t gc = g < G ? g : G - 1;  // tail lanes re-read the last group; they store nothing
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + gc * 128);
-    raw[p][0] = __builtin_nontemporal_load(src + j);
-    raw[p][1] = __builtin_nontemporal_load(src + j + 8);
+    if (!TAIL) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(x + gc * 128);
+      raw[p][0] = __builtin_nontemporal_load(src + j);
+      raw[p][1] = __builtin_nontemporal_load(src + j + 8);
+    } else {
+      const int64_t row = gc / Kg;
+      const int c0 = (int)(gc - row * Kg) * 128 + 8 * j;   // channels c0 .. c0+7 and c0+64 ..
+      const uint16_t* src = x + row * K;
+      raw[p][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + min(c0, K - 8)));
+      raw[p][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + min(c0 + 64, K - 8)));
+      if (c0 >= K) raw[p][0] = u32x4{0u, 0u, 0u, 0u};
+      if (c0 + 64 >= K) raw[p][1] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
 #pragma unroll
   for (int p = 0; p < ACT_PASSES; ++p) {
@@ -108,9 +129,12 @@ __device__ __forceinline__ void transpose4x4(const uint32_t r[4], uint32_t c[4])
   c[3] = __builtin_amdgcn_perm(p23h, p01h, 0x07060302u);
 }
 
+// The codes are [Np, Kp] (and wq_t [Kp, Np]), N and K rounded up to 128; in
+// the TAIL instantiation the rows past N and the channels past K read as +0.
+template <bool TAIL>
 __global__ __launch_bounds__(W_THREADS) void quant_weight_128x128_kernel(
     const uint16_t* __restrict__ w, uint8_t* __restrict__ wq, float* __restrict__ ws,
-    uint8_t* __restrict__ wq_t, int N, int K, int nb0) {
+    uint8_t* __restrict__ wq_t, int N, int K, int Np, int Kp, int nb0) {
   __shared__ float red[W_THREADS / 64];
   __shared__ __align__(16) uint8_t tile_t[128 * W_ROW_BYTES];
   const int t = threadIdx.x;
@@ -121,8 +145,15 @@ __global__ __launch_bounds__(W_THREADS) void quant_weight_128x128_kernel(
 
   u32x4 raw[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w + (row0 + i) * K + col0));
+  for (int i = 0; i < 8; ++i) {
+    if (!TAIL) {
+      raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w + (row0 + i) * K + col0));
+    } else {
+      const int64_t r = min(row0 + i, (int64_t)N - 1), c = min(col0, (int64_t)K - 8);
+      raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w + r * K + c));
+      if (row0 + i >= N || col0 >= K) raw[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
 
   float m = 0.0f;
 #pragma unroll
@@ -155,9 +186,9 @@ __global__ __launch_bounds__(W_THREADS) void quant_weight_128x128_kernel(
     code[i][0] = e4m3x4(q[0], q[1], q[2], q[3]);
     code[i][1] = e4m3x4(q[4], q[5], q[6], q[7]);
     __builtin_nontemporal_store(u32x2{code[i][0], code[i][1]},
-                                reinterpret_cast<u32x2*>(wq + (row0 + i) * K + col0));
+                                reinterpret_cast<u32x2*>(wq + (row0 + i) * Kp + col0));
   }
-  if (t == 0) ws[(int64_t)nb * (K / 128) + kb] = s;
+  if (t == 0) ws[(int64_t)nb * (Kp / 128) + kb] = s;
 
   if (wq_t != nullptr) {
     // Transpose the 8x8 byte tile: out[j] holds column c0+j, rows r0..r0+7.
@@ -188,7 +219,7 @@ __global__ __launch_bounds__(W_THREADS) void quant_weight_128x128_kernel(
       const u32x2 a = *reinterpret_cast<const u32x2*>(src);
       const u32x2 b = *reinterpret_cast<const u32x2*>(src + 8);
       __builtin_nontemporal_store(u32x4{a[0], a[1], b[0], b[1]},
-                                  reinterpret_cast<u32x4*>(wq_t + ((int64_t)kb * 128 + row) * N +
+                                  reinterpret_cast<u32x4*>(wq_t + ((int64_t)kb * 128 + row) * Np +
                                                            (int64_t)nb * 128 + 16 * seg));
     }
   }
@@ -203,12 +234,15 @@ __global__ __launch_bounds__(W_THREADS) void quant_weight_128x128_kernel(
 // across the 4 wavefronts through LDS. The codes go to an LDS tile
 // [128 channels][128 tokens] as 8-byte pieces and leave as 128-byte rows of
 // xq_t. A ragged token count M is padded: xq_t is [C, Mp] with Mp = M rounded
-// up to 128, and the tokens past M are read as +0 (code 0x00).
+// up to 128, and the tokens past M are read as +0 (code 0x00). In the TAIL
+// instantiation the last channel block is partial: its channels past C read
+// as +0 and their rows of xq_t / xs_t are not written.
 // ============================================================================
 constexpr int T_THREADS = 256;
 constexpr int T_CH = 128;
 constexpr int T_ROW_BYTES = 128 + 8;  // padded LDS row of the transposed code tile
 
+template <bool TAIL>
 __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ xq_t, float* __restrict__ xs_t,
     int M, int C, int cb0) {
@@ -227,13 +261,15 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
 
   // tokens past M (a ragged last block) read as +0: they leave the amax
   // alone and quantize to code 0x00
+  const int64_t cl = TAIL ? min(c0 + 8 * cc, (int64_t)C - 8) : c0 + 8 * cc;   // in-bounds chunk
+  const bool cvalid = !TAIL || c0 + 8 * cc < C;
   u32x4 raw[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t row = m0 + tr + i;
     raw[i] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(x + min(row, (int64_t)M - 1) * C + c0 + 8 * cc));
-    if (row >= M) raw[i] = u32x4{0u, 0u, 0u, 0u};
+        reinterpret_cast<const u32x4*>(x + min(row, (int64_t)M - 1) * C + cl));
+    if (row >= M || !cvalid) raw[i] = u32x4{0u, 0u, 0u, 0u};
   }
 
   float v[8][8];
@@ -258,7 +294,7 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
     p_sc[c] = d.sc;
     p_r[c] = d.r;
     p_mul[c] = d.xmul;
-    xs_t[(c0 + c) * (Mp / 128) + mb] = s;
+    if (!TAIL || c0 + c < C) xs_t[(c0 + c) * (Mp / 128) + mb] = s;
   }
   __syncthreads();
 
@@ -282,8 +318,9 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
     const uint8_t* src = tile + row * T_ROW_BYTES + 16 * seg;
     const u32x2 a = *reinterpret_cast<const u32x2*>(src);
     const u32x2 b = *reinterpret_cast<const u32x2*>(src + 8);
-    __builtin_nontemporal_store(u32x4{a[0], a[1], b[0], b[1]},
-                                reinterpret_cast<u32x4*>(xq_t + (c0 + row) * Mp + m0 + 16 * seg));
+    if (!TAIL || c0 + row < C)
+      __builtin_nontemporal_store(u32x4{a[0], a[1], b[0], b[1]},
+                                  reinterpret_cast<u32x4*>(xq_t + (c0 + row) * Mp + m0 + 16 * seg));
   }
 }
 
@@ -300,7 +337,10 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
 // group's amax is this thread's 8 channels reduced over the 16 lanes that
 // share its 8 tokens (one DPP row). M may be ragged: rows past M are read
 // clamped, produce +0, and only the padded transposed copy [C, Mp] (Mp = M
-// rounded up to 128) holds their 0x00 codes.
+// rounded up to 128) holds their 0x00 codes. In the TAIL instantiation the
+// last channel block is partial: channels past C produce +0, the 1x128 codes
+// are written padded ([M, Cp], Cp = C rounded up to 128, 0x00 past C), and the
+// transposed rows past C are not written.
 // ============================================================================
 enum EwOp { EW_COPY = 0, EW_RMSNORM = 1, EW_SWIGLU = 2 };
 
@@ -314,10 +354,10 @@ struct EwArgs {
   float* xs;
   uint8_t* xq_t;          // null: no 128x1 output
   float* xs_t;
-  int M, C, cb0;
+  int M, C, Cp, cb0;      // Cp: C rounded up to 128 (row length of xq)
 };
 
-template <int OP>
+template <int OP, bool TAIL>
 __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
   __shared__ float red[4][T_CH];
   __shared__ float p_sc[T_CH], p_r[T_CH], p_mul[T_CH];
@@ -332,14 +372,16 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
   const int64_t m0 = (int64_t)mb * 128;
   const int64_t c0 = (int64_t)cb * T_CH;
   const int C = a.C;
+  const int64_t cl = TAIL ? min(c0 + 8 * cc, (int64_t)C - 8) : c0 + 8 * cc;   // in-bounds chunk
+  const bool cvalid = !TAIL || c0 + 8 * cc < C;
 
   u32x4 raw[8], raw2[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t row = min(m0 + tr + i, (int64_t)a.M - 1);
-    raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x + row * C + c0 + 8 * cc));
+    raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x + row * C + cl));
     if (OP == EW_SWIGLU)
-      raw2[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x2 + row * C + c0 + 8 * cc));
+      raw2[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x2 + row * C + cl));
   }
 
   // The produced values are bf16 numbers; they stay packed (two per
@@ -351,7 +393,7 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
     for (int i = 0; i < 8; ++i) pv[i] = raw[i];
   } else if (OP == EW_RMSNORM) {
     float gm[8];
-    unpack8(*reinterpret_cast<const u32x4*>(a.gamma + c0 + 8 * cc), gm);
+    unpack8(*reinterpret_cast<const u32x4*>(a.gamma + cl), gm);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float r = a.rstd[min(m0 + tr + i, (int64_t)a.M - 1)];
@@ -380,11 +422,11 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
                     pack_bf16x2(yv[6], yv[7])};
     }
   }
-  // tokens past M (a ragged last block) are +0: they leave the 128x1 amax
-  // alone and quantize to code 0x00 in the padded transposed copy
+  // tokens past M (a ragged last block) and channels past C (a partial last
+  // channel block) are +0: they leave every amax alone and quantize to 0x00
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    if (m0 + tr + i >= a.M) pv[i] = u32x4{0u, 0u, 0u, 0u};
+    if (m0 + tr + i >= a.M || !cvalid) pv[i] = u32x4{0u, 0u, 0u, 0u};
   auto val = [&](int i, int e) -> float {
     const uint32_t w = pv[i][e >> 1];
     return (e & 1) ? bf16_hi(w) : bf16_lo(w);
@@ -393,7 +435,7 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t row = m0 + tr + i;
-      if (row < a.M) __builtin_nontemporal_store(pv[i], reinterpret_cast<u32x4*>(a.y + row * C + c0 + 8 * cc));
+      if (row < a.M && cvalid) __builtin_nontemporal_store(pv[i], reinterpret_cast<u32x4*>(a.y + row * C + c0 + 8 * cc));
     }
   }
 
@@ -412,8 +454,8 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
     const int64_t row = m0 + tr + i;
     if (row < a.M) {
       __builtin_nontemporal_store(u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])},
-                                  reinterpret_cast<u32x2*>(a.xq + row * C + c0 + 8 * cc));
-      if (cc == 0) a.xs[row * (C / 128) + cb] = s;
+                                  reinterpret_cast<u32x2*>(a.xq + row * a.Cp + c0 + 8 * cc));
+      if (cc == 0) a.xs[row * (a.Cp / 128) + cb] = s;
     }
   }
   if (a.xq_t == nullptr) return;   // uniform over the workgroup
@@ -438,7 +480,7 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
     p_sc[c] = d.sc;
     p_r[c] = d.r;
     p_mul[c] = d.xmul;
-    a.xs_t[(c0 + c) * (Mp / 128) + mb] = s;
+    if (!TAIL || c0 + c < C) a.xs_t[(c0 + c) * (Mp / 128) + mb] = s;
   }
   __syncthreads();
 #pragma unroll
@@ -459,8 +501,9 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
     const uint8_t* src = tile + row * T_ROW_BYTES + 16 * seg;
     const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
     const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
-    __builtin_nontemporal_store(u32x4{lo[0], lo[1], hi[0], hi[1]},
-                                reinterpret_cast<u32x4*>(a.xq_t + (c0 + row) * Mp + m0 + 16 * seg));
+    if (!TAIL || c0 + row < C)
+      __builtin_nontemporal_store(u32x4{lo[0], lo[1], hi[0], hi[1]},
+                                  reinterpret_cast<u32x4*>(a.xq_t + (c0 + row) * Mp + m0 + 16 * seg));
   }
 }
 
@@ -505,26 +548,40 @@ __global__ __launch_bounds__(256) void cast_f32_e4m3_kernel(const f32x4* __restr
 // ============================================================================
 // Launchers (shapes validated by the caller).
 // ============================================================================
+static int64_t groups128(int64_t n) { return (n + 127) / 128; }
+
 hipError_t launch_quant_act_1x128(const void* x, int64_t M, int64_t K, uint8_t* xq, float* xs,
                                   hipStream_t stream) {
-  const int64_t G = M * (K / 128);
+  const int64_t Kg = groups128(K);
+  const int64_t G = M * Kg;
   const int64_t blocks = (G + ACT_GROUPS_PER_BLOCK - 1) / ACT_GROUPS_PER_BLOCK;
+  const bool tail = K % 128 != 0;
   for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocks1D) {
     const int64_t nb = blocks - b0 < kMaxBlocks1D ? blocks - b0 : kMaxBlocks1D;
-    hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)nb), dim3(ACT_THREADS), 0, stream,
-                       static_cast<const uint16_t*>(x), xq, xs, G, b0);
+    if (tail)
+      hipLaunchKernelGGL(quant_act_1x128_kernel<true>, dim3((unsigned)nb), dim3(ACT_THREADS), 0, stream,
+                         static_cast<const uint16_t*>(x), xq, xs, G, b0, (int)K, (int)Kg);
+    else
+      hipLaunchKernelGGL(quant_act_1x128_kernel<false>, dim3((unsigned)nb), dim3(ACT_THREADS), 0, stream,
+                         static_cast<const uint16_t*>(x), xq, xs, G, b0, (int)K, (int)Kg);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_quant_weight_128x128(const void* w, int64_t N, int64_t K, uint8_t* wq, float* ws,
                                        uint8_t* wq_t, hipStream_t stream) {
-  const int64_t nbt = N / 128;
+  const int64_t nbt = groups128(N), kbt = groups128(K);
+  const bool tail = N % 128 != 0 || K % 128 != 0;
   for (int64_t y0 = 0; y0 < nbt; y0 += kMaxGridY) {
     const int64_t ny = nbt - y0 < kMaxGridY ? nbt - y0 : kMaxGridY;
-    hipLaunchKernelGGL(quant_weight_128x128_kernel, dim3((unsigned)(K / 128), (unsigned)ny),
-                       dim3(W_THREADS), 0, stream, static_cast<const uint16_t*>(w), wq, ws, wq_t,
-                       (int)N, (int)K, (int)y0);
+    const dim3 grid((unsigned)kbt, (unsigned)ny);
+    if (tail)
+      hipLaunchKernelGGL(quant_weight_128x128_kernel<true>, grid, dim3(W_THREADS), 0, stream,
+                         static_cast<const uint16_t*>(w), wq, ws, wq_t, (int)N, (int)K, (int)(nbt * 128),
+                         (int)(kbt * 128), (int)y0);
+    else
+      hipLaunchKernelGGL(quant_weight_128x128_kernel<false>, grid, dim3(W_THREADS), 0, stream,
+                         static_cast<const uint16_t*>(w), wq, ws, wq_t, (int)N, (int)K, (int)N, (int)K, (int)y0);
   }
   return hipGetLastError();
 }
@@ -533,24 +590,31 @@ hipError_t launch_quant_weight_128x128(const void* w, int64_t N, int64_t K, uint
 // pieces of the same xq_t rows), channel blocks along y.
 hipError_t launch_transpose_quant_128x1(const void* x, int64_t M, int64_t C, uint8_t* xq_t,
                                         float* xs_t, hipStream_t stream) {
-  const int64_t nc = C / T_CH;
+  const int64_t nc = groups128(C);
   for (int64_t y0 = 0; y0 < nc; y0 += kMaxGridY) {
     const int64_t ny = nc - y0 < kMaxGridY ? nc - y0 : kMaxGridY;
-    hipLaunchKernelGGL(transpose_quant_128x1_kernel, dim3((unsigned)((M + 127) / 128), (unsigned)ny),
-                       dim3(T_THREADS), 0, stream, static_cast<const uint16_t*>(x), xq_t, xs_t,
-                       (int)M, (int)C, (int)y0);
+    const dim3 grid((unsigned)((M + 127) / 128), (unsigned)ny);
+    if (C % 128)
+      hipLaunchKernelGGL(transpose_quant_128x1_kernel<true>, grid, dim3(T_THREADS), 0, stream,
+                         static_cast<const uint16_t*>(x), xq_t, xs_t, (int)M, (int)C, (int)y0);
+    else
+      hipLaunchKernelGGL(transpose_quant_128x1_kernel<false>, grid, dim3(T_THREADS), 0, stream,
+                         static_cast<const uint16_t*>(x), xq_t, xs_t, (int)M, (int)C, (int)y0);
   }
   return hipGetLastError();
 }
 
 template <int OP>
 static hipError_t launch_ew(EwArgs a, int64_t M, int64_t C, hipStream_t stream) {
-  const int64_t nc = C / T_CH;
+  const int64_t nc = groups128(C);
   for (int64_t y0 = 0; y0 < nc; y0 += kMaxGridY) {
     const int64_t ny = nc - y0 < kMaxGridY ? nc - y0 : kMaxGridY;
     a.cb0 = (int)y0;
-    hipLaunchKernelGGL(ew_quant_kernel<OP>, dim3((unsigned)((M + 127) / 128), (unsigned)ny), dim3(T_THREADS),
-                       0, stream, a);
+    const dim3 grid((unsigned)((M + 127) / 128), (unsigned)ny);
+    if (C % 128)
+      hipLaunchKernelGGL((ew_quant_kernel<OP, true>), grid, dim3(T_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL((ew_quant_kernel<OP, false>), grid, dim3(T_THREADS), 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -560,7 +624,7 @@ static EwArgs ew_args(const void* x, int64_t M, int64_t C, uint8_t* xq, float* x
   EwArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.xq = xq; a.xs = xs; a.xq_t = xq_t; a.xs_t = xs_t;
-  a.M = (int)M; a.C = (int)C;
+  a.M = (int)M; a.C = (int)C; a.Cp = (int)(groups128(C) * 128);
   return a;
 }
 

@@ -19,7 +19,9 @@ Every step runs in the library's HIP kernels through the C ABI:
               fp8_gemm_wgrad                      dW = dYq^T Xq
 Both paths quantize X with the same 1x128 rule and call the same GEMM, so a
 row of Y does not depend on whether gradients are tracked, on the other rows
-of the batch, or on the batch size.
+of the batch, or on the batch size. Feature counts that are not a multiple of
+128 end in partial groups; the FP8 codes are then padded to whole groups with
++0 codes and the GEMMs return the logical feature counts.
 """
 
 import torch
@@ -52,8 +54,9 @@ class FP8LinearFunction(torch.autograd.Function):
         # with +0 codes, and WGrad contracts over the padded length
         wq, ws, wq_t = codes.get(w)
         xq, xs, xq_t, xs_t = quantize_dual_1x128_128x1(x)
-        y = fp8_gemm_fwd(xq, xs, wq, ws)
+        y = fp8_gemm_fwd(xq, xs, wq, ws, n=w.shape[0])
         ctx.save_for_backward(xq_t, xs_t, wq_t, ws)
+        ctx.in_features = w.shape[1]
         return y
 
     @staticmethod
@@ -65,7 +68,7 @@ class FP8LinearFunction(torch.autograd.Function):
             dyq, dys, dyq_t, dys_t = quantize_dual_1x128_128x1(dy)
         else:
             dyq, dys = quantize_act_1x128(dy)
-        dx = fp8_gemm_dgrad(dyq, dys, wq_t, ws) if need_dx else None
+        dx = fp8_gemm_dgrad(dyq, dys, wq_t, ws, k=ctx.in_features) if need_dx else None
         dw = fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t) if need_dw else None
         return dx, dw, None
 
@@ -74,21 +77,21 @@ def fp8_linear_inference(x, w, codes):
     """The rollout path: Y = Xq Wq^T with no state kept for a backward pass."""
     wq, ws, _ = codes.get(w)
     xq, xs = quantize_act_1x128(x)
-    return fp8_gemm_fwd(xq, xs, wq, ws)
+    return fp8_gemm_fwd(xq, xs, wq, ws, n=w.shape[0])
 
 
 class FP8Linear(torch.nn.Module):
     """A bias-free linear layer (in_features -> out_features) on the FP8 flow.
 
     The weight is a bf16 parameter [out_features, in_features]; both feature
-    counts must be multiples of 128. Inputs are bf16 [..., in_features] on the
+    counts must be multiples of 8. Inputs are bf16 [..., in_features] on the
     GPU; leading dimensions are flattened into tokens.
     """
 
     def __init__(self, in_features, out_features, device="cuda", weight=None):
         super().__init__()
-        if in_features % 128 or out_features % 128:
-            raise ValueError("in_features and out_features must be multiples of 128")
+        if in_features % 8 or out_features % 8 or in_features <= 0 or out_features <= 0:
+            raise ValueError("in_features and out_features must be positive multiples of 8")
         if weight is None:
             weight = torch.empty((out_features, in_features), dtype=torch.bfloat16, device=device)
             torch.nn.init.normal_(weight, std=0.02)

@@ -38,6 +38,15 @@
  *     GEMM must be below 2^24 (the kernels address a tile's rows with 32-bit
  *     offsets). A call with a zero-sized output is a valid no-op.
  *   - Thread-safe and reentrant (no mutable global state).
+ *   - Channel dimensions (K, N, C) may be any multiple of 8 (so that bf16 rows
+ *     stay 16-byte aligned). Write Kp, Np for K, N rounded up to a multiple of
+ *     128, Kg = Kp/128, Ng = Np/128. When a dimension is not a multiple of 128,
+ *     its last group is partial: the group's amax (and so its scale) covers
+ *     the valid elements only, and the FP8 code tensors are padded along that
+ *     dimension to whole groups with code 0x00 (+0), which a GEMM contraction
+ *     reads as zero products. bf16 tensors keep their logical shape. (The
+ *     pages fix no layout for a partial group; for multiples of 128 nothing
+ *     changes.)
  */
 #ifndef FP8BSQ_H
 #define FP8BSQ_H
@@ -48,12 +57,12 @@
 extern "C" {
 #endif
 
-#define FP8BSQ_ABI_VERSION 5
+#define FP8BSQ_ABI_VERSION 6
 
 /* Status codes. */
 #define FP8BSQ_OK 0
 #define FP8BSQ_ERR_NULL 1      /* a required pointer is NULL                          */
-#define FP8BSQ_ERR_SHAPE 2     /* a dimension is negative, too large or not a multiple of 128 where required */
+#define FP8BSQ_ERR_SHAPE 2     /* a dimension is negative, too large, or not a multiple of 8 / 128 where required */
 #define FP8BSQ_ERR_ALIGN 3     /* a pointer is not 16-byte aligned                    */
 #define FP8BSQ_ERR_HIP 4       /* the HIP runtime reported an error at launch         */
 #define FP8BSQ_ERR_VALUE 5     /* a scalar argument is out of range (eps must be finite and >= 0) */
@@ -70,9 +79,10 @@ int fp8bsq_abi_version(void);
  * applied to dY before DGrad (backward GEMMs run in FP8, gradients arrive bf16).
  *
  *   x   in : bf16 [M, K]
- *   xq  out: E4M3 [M, K]           xq[m, k] = E4M3_RNE(fl32(x[m, k] / xs[m, k/128]))
- *   xs  out: fp32 [M, K/128]       xs[m, g] = scale of x[m, 128g : 128g+128]
- * Shape: K % 128 == 0; M >= 0 (any).
+ *   xq  out: E4M3 [M, Kp]          xq[m, k] = E4M3_RNE(fl32(x[m, k] / xs[m, k/128])),
+ *                                  0x00 for k >= K
+ *   xs  out: fp32 [M, Kg]          xs[m, g] = scale of x[m, 128g : min(128g+128, K)]
+ * Shape: K % 8 == 0; M >= 0 (any).
  */
 int quantize_act_1x128(const void* x, int64_t M, int64_t K,
                        uint8_t* xq, float* xs, void* stream);
@@ -83,11 +93,12 @@ int quantize_act_1x128(const void* x, int64_t M, int64_t K,
  * "Arquitectura Central": the bf16 master weights are what gets quantized.
  *
  *   w    in : bf16 [N, K]
- *   wq   out: E4M3 [N, K]
- *   ws   out: fp32 [N/128, K/128]  ws[i, j] = scale of block w[128i:128i+128, 128j:128j+128]
- *   wq_t out: E4M3 [K, N] or NULL  the byte transpose of wq (the DGrad operand;
+ *   wq   out: E4M3 [Np, Kp]        0x00 outside [0, N) x [0, K)
+ *   ws   out: fp32 [Ng, Kg]        ws[i, j] = scale of block w[128i : min(128i+128, N),
+ *                                                             128j : min(128j+128, K)]
+ *   wq_t out: E4M3 [Kp, Np] or NULL  the byte transpose of wq (the DGrad operand;
  *                                   a block's amax is transpose-invariant)
- * Shape: N % 128 == 0, K % 128 == 0.
+ * Shape: N % 8 == 0, K % 8 == 0.
  */
 int quantize_weight_128x128(const void* w, int64_t N, int64_t K,
                             uint8_t* wq, float* ws, uint8_t* wq_t, void* stream);
@@ -104,7 +115,8 @@ int quantize_weight_128x128(const void* w, int64_t N, int64_t K,
  * the transpose of x. A ragged M: the last group holds the remaining tokens
  * (its amax is theirs) and xq_t[c, m] = 0x00 (+0) for M <= m < Mp, so WGrad
  * can contract over Mp tokens. (The pages fix no layout for a ragged tail.)
- * Shape: C % 128 == 0; M any.
+ * C is not grouped here: xq_t has exactly C rows.
+ * Shape: C % 8 == 0; M any.
  */
 int transpose_quantize_128x1(const void* x, int64_t M, int64_t C,
                              uint8_t* xq_t, float* xs_t, void* stream);
@@ -119,11 +131,11 @@ int transpose_quantize_128x1(const void* x, int64_t M, int64_t C,
  * between forward and backward.
  *
  *   x    in : bf16 [M, K]
- *   xq   out: E4M3 [M, K],    xs   out: fp32 [M, K/128]   (as quantize_act_1x128)
+ *   xq   out: E4M3 [M, Kp],   xs   out: fp32 [M, Kg]      (as quantize_act_1x128)
  *   xq_t out: E4M3 [K, Mp],   xs_t out: fp32 [K, Mp/128]  (as transpose_quantize_128x1;
  *                                                          Mp = M rounded up to 128)
  * Every output is bit-identical to the corresponding single-output call.
- * Shape: K % 128 == 0; M any.
+ * Shape: K % 8 == 0; M any.
  */
 int quantize_dual_1x128_128x1(const void* x, int64_t M, int64_t K, uint8_t* xq, float* xs,
                               uint8_t* xq_t, float* xs_t, void* stream);
@@ -146,9 +158,10 @@ int quantize_dual_1x128_128x1(const void* x, int64_t M, int64_t K, uint8_t* xq, 
  * written. The sum of squares is accumulated in fp32 (per lane in order, then
  * a fixed butterfly over the wavefront), so rstd is deterministic; y may
  * differ from an exact evaluation by one bf16 unit in the last place.
- * Shape: K % 128 == 0; M any (the transposed outputs are [K, Mp] and
- * [K, Mp/128], Mp = M rounded up to 128, as transpose_quantize_128x1). Two kernel launches (the row statistics, then the quantizing
- * pass); rstd doubles as the buffer between them.
+ * Shape: K % 8 == 0; M any (xq is [M, Kp] and xs [M, Kg] as quantize_act_1x128;
+ * the transposed outputs are [K, Mp] and [K, Mp/128], Mp = M rounded up to
+ * 128, as transpose_quantize_128x1). Two kernel launches (the row statistics,
+ * then the quantizing pass); rstd doubles as the buffer between them.
  */
 int rmsnorm_quantize_1x128(const void* x, const void* gamma, float eps, int64_t M, int64_t K,
                            float* rstd, void* y, uint8_t* xq, float* xs, uint8_t* xq_t, float* xs_t,
@@ -169,8 +182,9 @@ int rmsnorm_quantize_1x128(const void* x, const void* gamma, float eps, int64_t 
  * The codes are those of the bf16 values h, bit for bit, whether or not h is
  * written; h may differ from an exact evaluation by one bf16 unit in the last
  * place.
- * Shape: N % 128 == 0; M any (the transposed outputs are [N, Mp] and
- * [N, Mp/128], Mp = M rounded up to 128, as transpose_quantize_128x1).
+ * Shape: N % 8 == 0; M any (hq is [M, Np] and hs [M, Ng] as quantize_act_1x128;
+ * the transposed outputs are [N, Mp] and [N, Mp/128], Mp = M rounded up to
+ * 128, as transpose_quantize_128x1).
  */
 int swiglu_quantize_1x128(const void* gate, const void* up, int64_t M, int64_t N, void* h,
                           uint8_t* hq, float* hs, uint8_t* hq_t, float* hs_t, void* stream);
@@ -181,11 +195,12 @@ int swiglu_quantize_1x128(const void* gate, const void* up, int64_t M, int64_t N
  * activations and 128x128 weights); "Arquitectura Central" (rollout and
  * training forward share this one flow).
  *
- *   xq in : E4M3 [M, K], xs in: fp32 [M, K/128]       (from quantize_act_1x128)
- *   wq in : E4M3 [N, K], ws in: fp32 [N/128, K/128]   (from quantize_weight_128x128)
+ *   xq in : E4M3 [M, Kp], xs in: fp32 [M, Kg]         (from quantize_act_1x128)
+ *   wq in : E4M3 [Np, Kp], ws in: fp32 [Ng, Kg]       (from quantize_weight_128x128)
  *   y  out: bf16 [M, N]
  *   y[m, n] = bf16( sum_kb xs[m,kb] * ws[n/128,kb] * sum_{k in kb} xq[m,k]*wq[n,k] )
- * Shape: N % 128 == 0, K % 128 == 0, M >= 0 (any), K < 2^24.
+ * M, N, K are the logical sizes. Shape: N % 8 == 0, K % 8 == 0, M >= 0 (any),
+ * Kp < 2^24.
  */
 int fp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                  void* y, int64_t M, int64_t N, int64_t K, void* stream);
@@ -195,12 +210,13 @@ int fp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const fl
  * Source: "Esquema de Cuantización", backward bullets (DGrad in FP8; bf16
  * gradients between operators).
  *
- *   dyq  in : E4M3 [M, N], dys in: fp32 [M, N/128]    (quantize_act_1x128 of dY)
- *   wq_t in : E4M3 [K, N]                              (wq_t of quantize_weight_128x128)
- *   ws   in : fp32 [N/128, K/128]                      (the same forward block scales)
+ *   dyq  in : E4M3 [M, Np], dys in: fp32 [M, Ng]      (quantize_act_1x128 of dY)
+ *   wq_t in : E4M3 [Kp, Np]                            (wq_t of quantize_weight_128x128)
+ *   ws   in : fp32 [Ng, Kg]                            (the same forward block scales)
  *   dx   out: bf16 [M, K]
  *   dx[m, k] = bf16( sum_nb dys[m,nb] * ws[nb,k/128] * sum_{n in nb} dyq[m,n]*wq_t[k,n] )
- * Shape: N % 128 == 0, K % 128 == 0, M >= 0 (any), N < 2^24.
+ * M, N, K are the logical sizes. Shape: N % 8 == 0, K % 8 == 0, M >= 0 (any),
+ * Np < 2^24.
  */
 int fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, const float* ws,
                    void* dx, int64_t M, int64_t N, int64_t K, void* stream);
@@ -214,7 +230,7 @@ int fp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wq_t, co
  *   xq_t  in : E4M3 [K, M], xs_t  in: fp32 [K, M/128]  (transpose_quantize_128x1 of X)
  *   dw    out: bf16 [N, K]
  *   dw[n, k] = bf16( sum_mb dys_t[n,mb] * xs_t[k,mb] * sum_{m in mb} dyq_t[n,m]*xq_t[k,m] )
- * Shape: M % 128 == 0, N % 128 == 0, K % 128 == 0, M < 2^24. For a ragged
+ * Shape: M % 128 == 0, N % 8 == 0, K % 8 == 0, M < 2^24. For a ragged
  * token count pass the padded Mp of the 128x1 quantizers' outputs (their
  * padded codes are +0 and contribute nothing).
  */

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_strerror(lib):
     lib.fp8bsq_abi_version.restype = ctypes.c_int
-    assert lib.fp8bsq_abi_version() == 5
+    assert lib.fp8bsq_abi_version() == 6
     lib.fp8bsq_strerror.restype = ctypes.c_char_p
     lib.fp8bsq_strerror.argtypes = [ctypes.c_int]
     for code in range(5):
@@ -56,7 +56,8 @@ MISALIGNED = P(0x10008)
 def test_quantizer_validation(lib):
     q = lib.quantize_act_1x128
     q.argtypes = [P, I64, I64, P, P, P]
-    assert q(FAKE, 4, 100, FAKE, FAKE, None) == 2          # K not a multiple of 128
+    assert q(FAKE, 4, 100, FAKE, FAKE, None) == 2          # K not a multiple of 8
+    assert q(None, 4, 200, FAKE, FAKE, None) == 1          # a partial channel group passes the shape check
     assert q(FAKE, -1, 128, FAKE, FAKE, None) == 2         # negative
     assert q(FAKE, 1 << 31, 128, FAKE, FAKE, None) == 2    # too large
     assert q(None, 4, 128, FAKE, FAKE, None) == 1          # null
@@ -65,11 +66,13 @@ def test_quantizer_validation(lib):
     w = lib.quantize_weight_128x128
     w.argtypes = [P, I64, I64, P, P, P, P]
     assert w(FAKE, 100, 128, FAKE, FAKE, None, None) == 2
+    assert w(FAKE, 136, 200, None, FAKE, None, None) == 1  # partial blocks pass the shape check
     assert w(FAKE, 128, 128, None, FAKE, None, None) == 1
     assert w(FAKE, 128, 128, FAKE, FAKE, MISALIGNED, None) == 3
     t = lib.transpose_quantize_128x1
     t.argtypes = [P, I64, I64, P, P, P]
-    assert t(FAKE, 64, 64, FAKE, FAKE, None) == 2          # C grouped by 128 (any M)
+    assert t(FAKE, 64, 60, FAKE, FAKE, None) == 2          # C a multiple of 8 (any M)
+    assert t(None, 64, 64, FAKE, FAKE, None) == 1          # C = 64 passes the shape check
     assert t(FAKE, (1 << 31) - 100, 128, FAKE, FAKE, None) == 2   # M rounded up to 128 is too large
     assert t(None, 64, 128, FAKE, FAKE, None) == 1         # a ragged M passes the shape check
     assert t(FAKE, 128, 128, FAKE, None, None) == 1
@@ -84,7 +87,8 @@ def test_dual_quantizer_validation(lib):
     d.argtypes = [P, I64, I64, P, P, P, P, P]
     d.restype = ctypes.c_int
     assert d(None, 64, 128, FAKE, FAKE, FAKE, FAKE, None) == 1        # a ragged M passes the shape check
-    assert d(FAKE, 128, 96, FAKE, FAKE, FAKE, FAKE, None) == 2        # channels grouped by 128
+    assert d(FAKE, 128, 100, FAKE, FAKE, FAKE, FAKE, None) == 2       # channels a multiple of 8
+    assert d(None, 128, 96, FAKE, FAKE, FAKE, FAKE, None) == 1        # 96 channels pass the shape check
     assert d(FAKE, -128, 128, FAKE, FAKE, FAKE, FAKE, None) == 2
     assert d(FAKE, 128, 128, FAKE, FAKE, None, FAKE, None) == 1       # every output is required
     assert d(FAKE, 128, 128, FAKE, FAKE, FAKE, MISALIGNED, None) == 3
@@ -95,7 +99,8 @@ def test_fused_producer_validation(lib):
     r = lib.rmsnorm_quantize_1x128
     r.argtypes = [P, P, ctypes.c_float, I64, I64, P, P, P, P, P, P, P]
     r.restype = ctypes.c_int
-    assert r(FAKE, FAKE, 1e-6, 3, 96, FAKE, None, FAKE, FAKE, None, None, None) == 2    # K % 128
+    assert r(FAKE, FAKE, 1e-6, 3, 100, FAKE, None, FAKE, FAKE, None, None, None) == 2   # K % 8
+    assert r(None, FAKE, 1e-6, 3, 96, FAKE, None, FAKE, FAKE, None, None, None) == 1    # K = 96 passes
     assert r(None, FAKE, 1e-6, 3, 128, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 1   # ragged M with transposed outputs
     assert r(FAKE, FAKE, -1.0, 3, 128, FAKE, None, FAKE, FAKE, None, None, None) == 5   # eps < 0
     assert r(FAKE, FAKE, float("nan"), 3, 128, FAKE, None, FAKE, FAKE, None, None, None) == 5
@@ -123,7 +128,8 @@ def test_gemm_validation(lib):
         f.argtypes = [P, P, P, P, P, I64, I64, I64, P]
         f.restype = ctypes.c_int
         assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 100, 128, None) == 2, name
-        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, 96, None) == 2, name
+        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, 100, None) == 2, name
+        assert f(FAKE, FAKE, None, FAKE, FAKE, 128, 136, 200, None) == 1, name  # partial groups pass
         assert f(FAKE, FAKE, None, FAKE, FAKE, 128, 128, 128, None) == 1, name
         assert f(FAKE, FAKE, FAKE, FAKE, MISALIGNED, 128, 128, 128, None) == 3, name
     f = lib.fp8_gemm_wgrad
@@ -146,7 +152,7 @@ def test_grouped_gemm_validation(lib):
     lib2 = fq.load_library()
     arr = (fq.GemmProblem * 3)()
     good = (0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
-    arr[1] = fq.GemmProblem(*good, 128, 128, 96)            # bad K: the whole call fails
+    arr[1] = fq.GemmProblem(*good, 128, 128, 100)           # bad K: the whole call fails
     arr[2] = fq.GemmProblem(*good, 128, 128, 128)
     for name, empty in (("fp8_gemm_fwd_grouped", (0, 128, 128)), ("fp8_gemm_dgrad_grouped", (0, 128, 128)),
                         ("fp8_gemm_wgrad_grouped", (128, 0, 128))):
