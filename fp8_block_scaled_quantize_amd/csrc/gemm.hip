@@ -316,8 +316,13 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
     const float* rsc = &rowsc[(kb >> 2) & 1][kb & 3];   // scale of row r at rsc[4 r]
 
     // First P fragment, then the Q fragments in the order the first slice
-    // uses them, so its first MFMA waits for two fragments only.
-    i32x8 pf0 = load_frag(tp, wi * C::WI + r16);
+    // uses them, so its first MFMA waits for two fragments only. The P
+    // fragments run PF_DEPTH slices ahead of their MFMAs (a ring of
+    // PF_DEPTH + 1), which hides the LDS latency of a slice behind the MFMAs
+    // of the PF_DEPTH slices before it.
+    constexpr int PF_DEPTH = 2;
+    i32x8 pring[PF_DEPTH + 1];
+    pring[0] = load_frag(tp, wi * C::WI + r16);
     i32x8 qf[SJ];
     float cj[SJ];
 #pragma unroll
@@ -331,6 +336,8 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
 #pragma unroll
       for (int b = 0; b < SJ; ++b) cj[b] *= psw;
     }
+#pragma unroll
+    for (int a = 1; a < PF_DEPTH; ++a) pring[a] = load_frag(tp, wi * C::WI + a * 16 + r16);
     // the next group of row scales goes out at the first step of each group
     if ((kb & 3) == 0 && kb + 4 < p.Kb) load_row_scales((kb >> 2) + 1);
 
@@ -351,7 +358,9 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
 #pragma unroll
         for (int r = 0; r < Q_INSTR / LOAD_SLICES; ++r) q_slab(al * (Q_INSTR / LOAD_SLICES) + r, kn, sn);
       }
-      const i32x8 pf = a == 0 ? pf0 : load_frag(tp, wi * C::WI + a * 16 + r16);
+      if (a + PF_DEPTH < SI)
+        pring[(a + PF_DEPTH) % (PF_DEPTH + 1)] = load_frag(tp, wi * C::WI + (a + PF_DEPTH) * 16 + r16);
+      const i32x8 pf = pring[a % (PF_DEPTH + 1)];
       f32x4 rs = zero;
       if (PS_ROW) {
         const int prow = C::BJ + wi * C::WI + a * 16 + 4 * g;
