@@ -80,14 +80,14 @@ struct GemmCfg {
   static constexpr int P_LOADS = BI * 8 / NT;                    // 16-byte loads per thread
   static constexpr int Q_LOADS = BJ * 8 / NT;
   static constexpr int ROWSC = BJ + (PS_ROW ? BI : 0);          // per-row scales per K step
-  static constexpr int BLKSC = PS_ROW ? 0 : BI / 128;            // 128x128-block P scales per K step
+  static constexpr int BLKSC = PS_ROW ? 0 : (BI + 127) / 128;    // 128x128-block P scales per K step
   static constexpr int BLKSC_PAD = BLKSC > 0 ? BLKSC : 1;
   static constexpr int TILE_BYTES = (BI + BJ) * 128;
   static_assert(BI * 8 % NT == 0 && BJ * 8 % NT == 0, "loads must divide evenly");
   static constexpr int ROW_PASSES = (ROWSC + NT - 1) / NT;      // per-row scales per thread
   static_assert(BLKSC <= 64 && BJ % 64 == 0 && NT % 64 == 0, "scale lanes");
   static_assert(PS_ROW || (128 % WI == 0), "a block-scaled wavefront must sit inside one 128-row block");
-  static_assert(BI % 128 == 0, "BI must be a multiple of 128");
+  static_assert(BI % 64 == 0 && (BI >= 128 || 128 % BI == 0), "a workgroup's P rows sit in whole 128-row blocks or inside one");
 };
 
 // Byte offset of 16-byte chunk `chunk` of tile row `row` (rows are 128 bytes).
@@ -306,7 +306,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
   // the first, so the two do not stall on copy issue at the same moments
   // (+4 % on WGrad, neutral elsewhere). The offset is a compile-time
   // constant so the unrolled slices stay free of branches.
-  constexpr int LOAD_SLICES_ = 4;   // slices over which a step's copies are spread
+  constexpr int LOAD_SLICES_ = (P_INSTR % 4 == 0 && Q_INSTR % 4 == 0) ? 4 : 2;   // slices over which a step's copies are spread
   auto main_loop = [&](auto copy_offset) {
   constexpr int OFF = decltype(copy_offset)::value;
   int st = 0;                       // stage of step kb
@@ -497,23 +497,31 @@ static hipError_t run_gemm_cfg(GemmParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Two tile configurations.
+// Three tile configurations. Every one reduces K in the same order (one MFMA
+// and one promotion per 128-long block, in order), so the choice changes no
+// output bit.
 //  large: 256 x 256 tile, 8 wavefronts (2 per SIMD) of 128 x 64, 2 LDS
 //         stages. (A 256 x 128 tile with one wavefront per SIMD and 3 stages
 //         measured slower: one wavefront cannot hide its own LDS latency.)
-//  small: 128 x 64 tile, 2 wavefronts of 64 x 64, 3 LDS stages (two
+//  small: 128 x 64 tile, 4 wavefronts of 64 x 32, 3 LDS stages (two
 //         workgroups per compute unit): for problems with fewer large tiles
 //         than compute units (decode-sized M, small outputs), where it
 //         measured 1.1-2.5x faster; more workgroups and a deeper prefetch.
+//  tiny:  64 x 64 tile, 4 wavefronts of 32 x 32, 3 LDS stages: when even the
+//         small tiles are too few (under two per compute unit), e.g. the
+//         long-contraction linears at 256 tokens, where the extra workgroups
+//         measured 10-25 % faster than the small tile.
 // The large one runs only where both output dimensions hold a whole tile, so
-// only the small one has a clamped-row (CLAMP) instantiation.
+// only the tiny one has a clamped-row (CLAMP) instantiation.
 template <bool PS_ROW>
 static hipError_t run_gemm(GemmParams p, hipStream_t stream) {
   const int64_t large_tiles = (int64_t)((p.I + 255) / 256) * ((p.J + 255) / 256);
   if (p.I >= 256 && p.J >= 256 && large_tiles >= 256)
     return run_gemm_cfg<2, 4, 8, 4, PS_ROW, 2, false>(p, stream);
-  if (p.I >= 128 && p.J >= 64) return run_gemm_cfg<2, 1, 4, 4, PS_ROW, 3, false>(p, stream);
-  return run_gemm_cfg<2, 1, 4, 4, PS_ROW, 3, true>(p, stream);
+  const int64_t small_tiles = (int64_t)((p.I + 127) / 128) * ((p.J + 63) / 64);
+  if (p.I >= 128 && p.J >= 64 && small_tiles >= 512) return run_gemm_cfg<2, 2, 4, 2, PS_ROW, 3, false>(p, stream);
+  if (p.I >= 64 && p.J >= 64) return run_gemm_cfg<2, 2, 2, 2, PS_ROW, 3, false>(p, stream);
+  return run_gemm_cfg<2, 2, 2, 2, PS_ROW, 3, true>(p, stream);
 }
 
 template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
@@ -537,7 +545,8 @@ static hipError_t run_grouped_cfg(const GemmParams* probs, int count, hipStream_
 }
 
 // One configuration for the whole group: the large one when every problem
-// qualifies for it and the group fills the chip, else the small one.
+// qualifies for it and the group fills the chip, else the small one (with
+// clamped rows when some problem is smaller than one small tile).
 template <bool PS_ROW>
 static hipError_t run_grouped(const GemmParams* probs, int count, hipStream_t stream) {
   bool large_ok = true, small_ok = true;
@@ -549,8 +558,8 @@ static hipError_t run_grouped(const GemmParams* probs, int count, hipStream_t st
     large_tiles += (int64_t)((q.I + 255) / 256) * ((q.J + 255) / 256);
   }
   if (large_ok && large_tiles >= 256) return run_grouped_cfg<2, 4, 8, 4, PS_ROW, 2, false>(probs, count, stream);
-  if (small_ok) return run_grouped_cfg<2, 1, 4, 4, PS_ROW, 3, false>(probs, count, stream);
-  return run_grouped_cfg<2, 1, 4, 4, PS_ROW, 3, true>(probs, count, stream);
+  if (small_ok) return run_grouped_cfg<2, 2, 4, 2, PS_ROW, 3, false>(probs, count, stream);
+  return run_grouped_cfg<2, 2, 4, 2, PS_ROW, 3, true>(probs, count, stream);
 }
 
 // Operand roles. All three run D[i][j] = sum_k P[i,k] Q[j,k], written to out[j][i].
