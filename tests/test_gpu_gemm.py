@@ -274,6 +274,23 @@ def test_identity_weight():
     _assert_close(host_bits(dx), ref, "dgrad identity")
 
 
+@pytest.mark.parametrize("role", ["fwd", "dgrad"])
+def test_rows_identical_across_tile_configurations(role):
+    # Every tile configuration reduces K in the same order, so a token's output
+    # row does not depend on how many tokens share the call. With N = K = 4096:
+    # 4096 tokens run the 256x256 tiles, 1024 the 128x64 tiles, 256 and 64 the
+    # 64x64 tiles, 17 the 64x64 tiles with clamped rows.
+    M, N, K = 4096, 4096, 4096
+    note(f"{role}: rows of a {M}-token call vs 1024/256/64/17-token calls (every tile configuration)")
+    a, as_, b, bs = _quantized_problem(role, M, N, K, seed=77)
+    f = getattr(fq, f"fp8_gemm_{role}")
+    full = f(a, as_, b, bs)
+    parts = {rows: f(a[:rows].contiguous(), as_[:rows].contiguous(), b, bs) for rows in (1024, 256, 64, 17)}
+    torch.cuda.synchronize()
+    for rows, part in parts.items():
+        assert torch.equal(part, full[:rows]), f"{role}: {rows} rows differ from the {M}-row call"
+
+
 def test_gemm_determinism():
     note("GEMMs: repeated calls give identical bytes")
     x = inputs.bf16_normal_device((2048, 4096), 1.0, 0.01, seed=21)
