@@ -38,6 +38,8 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s (fwd/DGrad/WGrad), % of FP8 MFMA peak"
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA, published
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "qwen25_32b_linears_m32768"
+ROTATE_BYTES = 640 << 20        # > 256 MB last-level cache + 8 x 4 MB L2, with margin
+MAX_SETS = 32
 
 
 def parse():
@@ -53,6 +55,12 @@ def parse():
                     help="one WGrad launch per linear instead of one grouped launch for all of them")
     ap.add_argument("--separate-quant", action="store_true",
                     help="quantize X and dY with the single-output kernels (two reads each)")
+    ap.add_argument("--weights-prequantized", action="store_true",
+                    help="quantize the weights once per input set outside the timed step "
+                         "(rollout: weights change once per optimizer update)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input/weight sets rotated between steps (0: enough that one rotation "
+                         "touches more than the 256 MB last-level cache plus L2)")
     ap.add_argument("--traffic-from", default=None,
                     help="JSON with measured HBM bytes per launch of the dominant kernel")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -60,6 +68,8 @@ def parse():
                          "FETCH_SIZE / WRITE_SIZE calibrate the HBM counters")
     ap.add_argument("--summarize-trace", metavar="CSV", default=None,
                     help="host only: per (kernel, grid) average durations from a rocprofv3 kernel trace")
+    ap.add_argument("--summarize-runs", metavar="JSON", nargs="+", default=None,
+                    help="print a markdown table of the launches of bench.py result lines (files)")
     ap.add_argument("--summarize-counters", metavar="CSV", nargs="+", default=None,
                     help="host only: per (kernel, grid) averages of rocprofv3 --pmc counter CSVs")
     return ap.parse_args()
@@ -290,8 +300,30 @@ def summarize_counters(paths):
         print(f"{k:80s} {g:>10s} {c:>12s} {len(vals):10d} {sum(vals)/len(vals):14.1f}")
 
 
+def summarize_runs(paths):
+    """Markdown table of the per-launch timings of bench.py result lines."""
+    for path in paths:
+        r = json.loads(open(path).read().strip().splitlines()[-1])
+        c = r["config"]
+        print(f"### {c['workload']}  ({', '.join(c['passes'])}; {r['input_sets']} input set(s); "
+              f"weights {r.get('weights', 'quantized inside the step')})\n")
+        print(f"step {r['ms_per_step']} ms, {r['value']} TFLOP/s over the step, GEMMs alone "
+              f"{r['gemm_only_tflops']} TFLOP/s\n")
+        print("| launch | ms | rate | of peak |\n|---|---|---|---|")
+        for key, k in r["kernels"].items():
+            if "tflops" in k:
+                gbs = f", {k['gbs']} GB/s ({100 * k['gbs'] / PEAK_HBM_GBS:.1f} % HBM)" if "gbs" in k else ""
+                print(f"| {key} | {k['ms']} | {k['tflops']} TFLOP/s{gbs} | {100 * k['frac_fp8_peak']:.1f} % FP8 |")
+            else:
+                print(f"| {key} | {k['ms']} | {k['gbs']} GB/s | {100 * k['frac_hbm_peak']:.1f} % HBM |")
+        print()
+
+
 def main():
     args = parse()
+    if args.summarize_runs:
+        summarize_runs(args.summarize_runs)
+        return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
         return
@@ -314,21 +346,37 @@ def main():
     wl = inputs.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     print(f"[bench] workload {args.workload}: generating inputs", file=sys.stderr, flush=True)
-    layers = [Linear(lin, wl["passes"], 1000 + 17 * i, fq, inputs, torch, dual=not args.separate_quant)
-              for i, lin in enumerate(wl["linears"])]
-    grouped = not args.no_grouped and "wgrad" in wl["passes"] and len(layers) > 1
-    for layer in layers:
-        layer.defer_wgrad = grouped
-    launches = [l for layer in layers for l in layer.launches()]
-    if grouped:
-        # the WGrads of all linears in one launch (they are independent of the
-        # rest of the step; a backward pass can defer them to the end)
-        probs = [layer.wgrad_problem() for layer in layers]
-        outs = [p[1] for p in probs]
-        ops = [p[0] for p in probs]
-        names = "+".join(layer.name for layer in layers)
-        launches.append(("gemm_wgrad", f"wgrad_grouped[{names}]", sum(p[2] for p in probs),
-                         sum(p[3] for p in probs), lambda: fq.fp8_gemm_wgrad_grouped(ops, outs)))
+    grouped = not args.no_grouped and "wgrad" in wl["passes"] and len(wl["linears"]) > 1
+
+    def build_step(seed):
+        layers = [Linear(lin, wl["passes"], seed + 17 * i, fq, inputs, torch, dual=not args.separate_quant)
+                  for i, lin in enumerate(wl["linears"])]
+        for layer in layers:
+            layer.defer_wgrad = grouped
+        steps = [l for layer in layers for l in layer.launches()]
+        if args.weights_prequantized:
+            for l in [l for l in steps if l[0] == "quant_weight"]:
+                l[4]()
+            steps = [l for l in steps if l[0] != "quant_weight"]
+        if grouped:
+            # the WGrads of all linears in one launch (they are independent of the
+            # rest of the step; a backward pass can defer them to the end)
+            probs = [layer.wgrad_problem() for layer in layers]
+            outs = [p[1] for p in probs]
+            ops = [p[0] for p in probs]
+            names = "+".join(layer.name for layer in layers)
+            steps.append(("gemm_wgrad", f"wgrad_grouped[{names}]", sum(p[2] for p in probs),
+                          sum(p[3] for p in probs), lambda: fq.fp8_gemm_wgrad_grouped(ops, outs)))
+        return steps
+
+    # Small workloads rotate through independent input sets, so that no step
+    # finds its operands in the 256 MB last-level cache from the step before.
+    sets = [build_step(1000)]
+    step_bytes = sum(l[3] for l in sets[0])
+    nsets = args.rotate if args.rotate > 0 else min(MAX_SETS, -(-ROTATE_BYTES // step_bytes))
+    for r in range(1, nsets):
+        sets.append(build_step(1000 + 7919 * r))
+    launches = sets[0]
     torch.cuda.synchronize()
     if args.calibrate_copy:
         cx = torch.ones((1 << 29,), dtype=torch.bfloat16, device="cuda")    # 1 GiB
@@ -337,8 +385,8 @@ def main():
         torch.cuda.synchronize()
         del cx, cy
 
-    for s in range(args.warmup):
-        for _, _, _, _, fn in launches:
+    for s in range(max(args.warmup, nsets)):
+        for _, _, _, _, fn in sets[s % nsets]:
             fn()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
@@ -349,7 +397,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        for i, (_, _, _, _, fn) in enumerate(launches):
+        for i, (_, _, _, _, fn) in enumerate(sets[s % nsets]):
             ev[s][i][0].record(stream)
             fn()
             ev[s][i][1].record(stream)
@@ -372,7 +420,8 @@ def main():
         if p["flops"]:
             tf = p["flops"] / (p["ms"] * 1e-3) / 1e12
             kernels[p["key"]] = {"ms": round(p["ms"], 4), "tflops": round(tf, 1),
-                                 "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+                                 "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                                 "gbs": round(p["bytes"] / (p["ms"] * 1e-3) / 1e9, 1)}
         else:
             gbs = p["bytes"] / (p["ms"] * 1e-3) / 1e9
             kernels[p["key"]] = {"ms": round(p["ms"], 4), "gbs": round(gbs, 1),
@@ -415,6 +464,9 @@ def main():
         "quant_ms_per_step": round(quant_ms, 3),
         "quantizers": "separate" if args.separate_quant else "dual",
         "wgrad_launch": "grouped" if grouped else "per linear",
+        "input_sets": nsets,
+        "weights": "quantized once per input set, outside the step" if args.weights_prequantized
+                   else "quantized inside the step",
         "roofline": roof,
         "kernels": kernels,
     }
