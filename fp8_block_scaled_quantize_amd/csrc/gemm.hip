@@ -20,15 +20,17 @@
 //
 // Each 128-long K block is exactly one v_mfma_f32_16x16x128_f8f6f4 per 16x16
 // output tile, so the block's partial sum comes out of a single MFMA with a
-// zero accumulator and is promoted into the fp32 running sum with one FMA per
-// element: acc += partial * ps * qs. In the MFMA result layout a lane holds
-// four consecutive i of one j, so the Q scale is one value per lane and a
-// block P scale is uniform over the wavefront.
+// zero accumulator and is promoted into the fp32 running sum,
+// acc += partial * ps * qs: one FMA per element where the P scale is per
+// 128x128 block (forward, DGrad), a multiply and an FMA where both scales are
+// per row (WGrad). In the MFMA result layout a lane holds four consecutive i
+// of one j, so the Q scale is one value per lane and a block P scale is
+// uniform over the wavefront.
 //
 // Tiles: a workgroup owns a BI x BJ output tile and walks K in 128-byte steps.
-// Both operand tiles of a step are staged in LDS (double-buffered) with their
-// 16-byte chunks XOR-swizzled by row so that the MFMA fragment reads are free
-// of bank conflicts. Workgroups are mapped to tiles so that each XCD works on
+// Both operand tiles of a step are staged in LDS (two or three stages) with
+// their 16-byte chunks XOR-swizzled by row so that the MFMA fragment reads are
+// free of bank conflicts. Workgroups are mapped to tiles so that each XCD works on
 // a compact band of the output (its own L2), in groups along i.
 #include "device_common.h"
 #include "launch.h"
