@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--weights-prequantized", action="store_true",
                     help="quantize the weights once per input set outside the timed step "
                          "(rollout: weights change once per optimizer update)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph (one graph per input set) and "
+                         "replayed: graph_ms_per_step")
     ap.add_argument("--rotate", type=int, default=0,
                     help="input/weight sets rotated between steps (0: enough that one rotation "
                          "touches more than the 256 MB last-level cache plus L2)")
@@ -405,6 +408,34 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
+    graph_ms = None
+    if args.graph:
+        # The same launches captured once per input set and replayed: what a
+        # launch-bound step (decode) costs without per-launch host overhead.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for st in sets:
+                for _, _, _, _, fn in st:
+                    fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for st in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _, _, _, _, fn in st:
+                    fn()
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            graphs[s % nsets].replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
     # Per-launch average durations (ms) from the HIP events.
     per = []
     for i, (kind, key, flops, nbytes, _) in enumerate(launches):
@@ -465,6 +496,7 @@ def main():
         "quantizers": "separate" if args.separate_quant else "dual",
         "wgrad_launch": "grouped" if grouped else "per linear",
         "input_sets": nsets,
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "weights": "quantized once per input set, outside the step" if args.weights_prequantized
                    else "quantized inside the step",
         "roofline": roof,
