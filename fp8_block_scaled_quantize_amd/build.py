@@ -3,7 +3,9 @@
     python -m fp8_block_scaled_quantize_amd.build
 
 Compiles every csrc/*.hip to an object file, then links one shared library
-next to this file. Flags:
+next to this file; also builds the stand-alone GPU check programs under
+tests/gpu (each tests/gpu/<name>.hip -> tests/gpu/<name>), which GPU tests run.
+Flags:
   --offload-arch=gfx950                  MI355X only
   -O3 -std=c++17 -fPIC
   -fhip-fp32-correctly-rounded-divide-sqrt   IEEE fp32 division for the scales
@@ -38,6 +40,18 @@ COMMON_FLAGS = [
 ]
 
 
+# Stand-alone GPU check programs that tests run (not part of the library).
+CHECKS_DIR = os.path.join(ROOT, "tests", "gpu")
+
+
+def check_programs():
+    """(source, executable) pairs of the HIP check programs under tests/gpu."""
+    if not os.path.isdir(CHECKS_DIR):
+        return []
+    return [(os.path.join(CHECKS_DIR, f), os.path.join(CHECKS_DIR, f[:-4]))
+            for f in sorted(os.listdir(CHECKS_DIR)) if f.endswith(".hip")]
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
@@ -58,6 +72,8 @@ def build(verbose=False):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
         objs.append(obj)
         cmds.append([HIPCC, *COMMON_FLAGS, "-c", src, "-o", obj])
+    for src, exe in check_programs():
+        cmds.append([HIPCC, *COMMON_FLAGS, src, "-o", exe])
     with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():

@@ -42,9 +42,20 @@ __device__ __forceinline__ float clamp448(float q) {
 
 // Four fp32 values -> four E4M3 bytes (value a in the lowest byte).
 // v_cvt_pk_fp8_f32 on gfx950 converts to OCP E4M3 with round-to-nearest-even.
+// This form clamps first and takes any |v| <= 464.
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   int v = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
   v = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), v, true);
+  return (uint32_t)v;
+}
+
+// The same for quotients, which always have |q| < 449: on gfx950 the
+// converter gives, for every fp32 v with |v| < 449 (both signs, checked
+// exhaustively on the GPU), the byte it gives for clamp448(v), so the clamp
+// (two VALU operations per element) is left out.
+__device__ __forceinline__ uint32_t e4m3x4_q(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
   return (uint32_t)v;
 }
 
@@ -78,6 +89,12 @@ __device__ __forceinline__ GroupDiv group_div(float amax, float s) {
   g.r = 1.0f / g.sc;
   return g;
 }
+
+// True on every lane when some lane of the wavefront holds a tiny group
+// (xmul != 1): the pre-scaling multiply runs only then, so the branch is
+// uniform and the common case skips it (x * 1 is x, so either way the
+// quotient is the same).
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 __device__ __forceinline__ float quotient(float x, float sc, float r) {
   const float q0 = x * r;

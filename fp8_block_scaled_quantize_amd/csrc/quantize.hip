@@ -94,8 +94,8 @@ __global__ __launch_bounds__(ACT_THREADS) void quant_act_1x128_kernel(
     float q[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) q[i] = quotient(v[i], d.sc, d.r);
-    const u32x2 lo = u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
-    const u32x2 hi = u32x2{e4m3x4(q[8], q[9], q[10], q[11]), e4m3x4(q[12], q[13], q[14], q[15])};
+    const u32x2 lo = u32x2{e4m3x4_q(q[0], q[1], q[2], q[3]), e4m3x4_q(q[4], q[5], q[6], q[7])};
+    const u32x2 hi = u32x2{e4m3x4_q(q[8], q[9], q[10], q[11]), e4m3x4_q(q[12], q[13], q[14], q[15])};
     const int64_t g = grp[p];
     if (g < G) {
       u32x2* dst = reinterpret_cast<u32x2*>(xq + g * 128);
@@ -183,8 +183,8 @@ __global__ __launch_bounds__(W_THREADS) void quant_weight_128x128_kernel(
     float q[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = quotient(v[e], d.sc, d.r);
-    code[i][0] = e4m3x4(q[0], q[1], q[2], q[3]);
-    code[i][1] = e4m3x4(q[4], q[5], q[6], q[7]);
+    code[i][0] = e4m3x4_q(q[0], q[1], q[2], q[3]);
+    code[i][1] = e4m3x4_q(q[4], q[5], q[6], q[7]);
     __builtin_nontemporal_store(u32x2{code[i][0], code[i][1]},
                                 reinterpret_cast<u32x2*>(wq + (row0 + i) * Kp + col0));
   }
@@ -242,6 +242,29 @@ constexpr int T_THREADS = 256;
 constexpr int T_CH = 128;
 constexpr int T_ROW_BYTES = 128 + 8;  // padded LDS row of the transposed code tile
 
+// Workgroup order of the 128x1 and dual kernels (grid [token blocks,
+// channel blocks]). The hardware deals workgroup ids round-robin over the 8
+// XCDs; here each run of 256 ids is renumbered so that every XCD takes 32
+// consecutive token blocks of one channel block, one after another. The 4-byte
+// scale stores of those 32 workgroups then land in the same 128-byte lines of
+// the transposed scales (32 consecutive token blocks of one channel) and, one
+// run later, beside each other in the row scales, while the lines are still in
+// that XCD's L2, so the lines go out to HBM merged instead of as dozens of
+// partial writes (5-9 % faster, same bytes). Ids past the last whole run of
+// 256 keep their order. Every tensor has fewer than 2^40 elements and a
+// workgroup covers 2^14, so the ids fit in int.
+__device__ __forceinline__ void token_major_block(int& mb, int& cbi) {
+  const int nx = (int)gridDim.x, n = nx * (int)gridDim.y;
+  const int bid = (int)blockIdx.x + (int)blockIdx.y * nx;
+  int L = bid;
+  if (bid < (n / 256) * 256) {
+    const int xcd = bid % 8, k = bid / 8;
+    L = (k / 32) * 256 + xcd * 32 + (k % 32);
+  }
+  mb = L % nx;
+  cbi = L / nx;
+}
+
 template <bool TAIL>
 __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ xq_t, float* __restrict__ xs_t,
@@ -254,9 +277,10 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
   const int cc = t & 15;          // channel chunk: channels 8cc .. 8cc+7 of the tile
   const int tr = 8 * (t >> 4);    // first token of this thread's eight
   const int wave = t >> 6, lane = t & 63;
-  const int mb = blockIdx.x;
+  int mb, cbi;
+  token_major_block(mb, cbi);
   const int64_t m0 = (int64_t)mb * 128;
-  const int64_t c0 = ((int64_t)cb0 + blockIdx.y) * T_CH;
+  const int64_t c0 = ((int64_t)cb0 + cbi) * T_CH;
   const int64_t Mp = ((int64_t)M + 127) & ~(int64_t)127;   // padded token count of xq_t
 
   // tokens past M (a ragged last block) read as +0: they leave the amax
@@ -302,11 +326,17 @@ __global__ __launch_bounds__(T_THREADS) void transpose_quant_128x1_kernel(
   for (int e = 0; e < 8; ++e) {
     const int c = 8 * cc + e;
     const float sc = p_sc[c], r = p_r[c], mul = p_mul[c];
-    float q[8];
+    float xv[8], q[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = quotient(v[i][e] * mul, sc, r);
+    for (int i = 0; i < 8; ++i) xv[i] = v[i][e];
+    if (wave_any(mul != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xv[i] *= mul;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = quotient(xv[i], sc, r);
     *reinterpret_cast<u32x2*>(tile + c * T_ROW_BYTES + tr) =
-        u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
+        u32x2{e4m3x4_q(q[0], q[1], q[2], q[3]), e4m3x4_q(q[4], q[5], q[6], q[7])};
   }
   __syncthreads();
 
@@ -367,8 +397,9 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
   const int cc = t & 15;          // channel chunk: channels 8cc .. 8cc+7 of the tile
   const int tr = 8 * (t >> 4);    // first token of this thread's eight
   const int wave = t >> 6, lane = t & 63;
-  const int mb = blockIdx.x;
-  const int cb = a.cb0 + (int)blockIdx.y;
+  int mb, cbi;
+  token_major_block(mb, cbi);
+  const int cb = a.cb0 + cbi;
   const int64_t m0 = (int64_t)mb * 128;
   const int64_t c0 = (int64_t)cb * T_CH;
   const int C = a.C;
@@ -448,12 +479,18 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
     m = max16(m);
     const float s = group_scale(m);
     const GroupDiv d = group_div(m, s);
-    float q[8];
+    float xv[8], q[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = quotient(val(i, e) * d.xmul, d.sc, d.r);
+    for (int e = 0; e < 8; ++e) xv[e] = val(i, e);
+    if (wave_any(d.xmul != 1.0f)) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[e] *= d.xmul;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = quotient(xv[e], d.sc, d.r);
     const int64_t row = m0 + tr + i;
     if (row < a.M) {
-      __builtin_nontemporal_store(u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])},
+      __builtin_nontemporal_store(u32x2{e4m3x4_q(q[0], q[1], q[2], q[3]), e4m3x4_q(q[4], q[5], q[6], q[7])},
                                   reinterpret_cast<u32x2*>(a.xq + row * a.Cp + c0 + 8 * cc));
       if (cc == 0) a.xs[row * (a.Cp / 128) + cb] = s;
     }
@@ -487,11 +524,17 @@ __global__ __launch_bounds__(T_THREADS) void ew_quant_kernel(EwArgs a) {
   for (int e = 0; e < 8; ++e) {
     const int c = 8 * cc + e;
     const float sc = p_sc[c], r = p_r[c], mul = p_mul[c];
-    float q[8];
+    float xv[8], q[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = quotient(val(i, e) * mul, sc, r);
+    for (int i = 0; i < 8; ++i) xv[i] = val(i, e);
+    if (wave_any(mul != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xv[i] *= mul;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = quotient(xv[i], sc, r);
     *reinterpret_cast<u32x2*>(tile + c * T_ROW_BYTES + tr) =
-        u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
+        u32x2{e4m3x4_q(q[0], q[1], q[2], q[3]), e4m3x4_q(q[4], q[5], q[6], q[7])};
   }
   __syncthreads();
 #pragma unroll

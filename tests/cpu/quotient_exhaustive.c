@@ -16,7 +16,10 @@
  * be enumerated: about 1.07e9 pairs with both signs of x. For each pair the
  * signed E4M3 byte of q must equal the byte of fl32(x / s), and the float32
  * bits must agree whenever |x / s| >= 2^-11 (below that both encode to a
- * signed zero). Prints counts and exits non-zero on any mismatch.
+ * signed zero). It also records the largest |q|, which must stay below 449:
+ * the kernels hand q to the hardware E4M3 converter without clamping it to
+ * +-448, and the converter matches clamp-then-convert for every |v| < 449.
+ * Prints counts and exits non-zero on any mismatch or a larger |q|.
  *
  * Build: gcc -O2 -mfma -ffp-contract=off -fopenmp quotient_exhaustive.c -lm
  */
@@ -43,8 +46,9 @@ static uint8_t enc(float v) {
 
 int main(void) {
     long long pairs = 0, byte_bad = 0, f32_bad = 0;
+    float maxq = 0.0f;
     const float two64 = 18446744073709551616.0f;
-#pragma omp parallel for schedule(dynamic, 64) reduction(+ : pairs, byte_bad, f32_bad)
+#pragma omp parallel for schedule(dynamic, 64) reduction(+ : pairs, byte_bad, f32_bad) reduction(max : maxq)
     for (uint32_t ab = 1; ab < 0x7F80u; ++ab) {
         float amax = bf16(ab);
         float s = amax / 448.0f;
@@ -64,11 +68,13 @@ int main(void) {
                 float q = fmaf(-d, r, q0);
                 float ref = x / s;
                 ++pairs;
+                if (fabsf(q) > maxq) maxq = fabsf(q);
                 if (enc(q) != enc(ref)) ++byte_bad;
                 if (fabsf(ref) >= 0.00048828125f && bits(q) != bits(ref)) ++f32_bad;
             }
         }
     }
-    printf("pairs=%lld byte_mismatch=%lld f32_mismatch=%lld\n", pairs, byte_bad, f32_bad);
-    return (byte_bad || f32_bad) ? 1 : 0;
+    printf("pairs=%lld byte_mismatch=%lld f32_mismatch=%lld max_abs_q=%.9g\n", pairs, byte_bad, f32_bad,
+           (double)maxq);
+    return (byte_bad || f32_bad || !(maxq < 449.0f)) ? 1 : 0;
 }
