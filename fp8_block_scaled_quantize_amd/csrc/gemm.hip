@@ -543,7 +543,7 @@ static hipError_t run_gemm_cfg(GemmParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Three tile configurations. Every one reduces K in the same order (one MFMA
+// Four tile configurations. Every one reduces K in the same order (one MFMA
 // and one promotion per 128-long block, in order), so the choice changes no
 // output bit.
 //  large: 256 x 256 tile, 8 wavefronts (2 per SIMD) of 128 x 64, 2 LDS
@@ -557,13 +557,28 @@ static hipError_t run_gemm_cfg(GemmParams p, hipStream_t stream) {
 //         small tiles are too few (under two per compute unit), e.g. the
 //         long-contraction linears at 256 tokens, where the extra workgroups
 //         measured 10-25 % faster than the small tile.
-// The large one runs only where both output dimensions hold a whole tile, so
-// only the tiny one has a clamped-row (CLAMP) instantiation.
+//  medium: 256 x 128 tile, 8 wavefronts of 128 x 32, 3 LDS stages (148-156
+//         KB, one workgroup per compute unit): instead of the large tile when
+//         the large tiles end just past a whole round of the 256 compute
+//         units (320 tiles are 1.25 rounds: the last round leaves 3/4 of the
+//         chip idle). Per FLOP it measured 4-9 % slower than the large tile;
+//         it is chosen when rounds x cost per tile is lower, with a medium
+//         tile costing 0.54 of a large one (measured on the linears of a
+//         32B-parameter model at 4096 tokens: 11-16 % faster where the large
+//         tiles number 320, slower at 400, 448 and 1728).
+// The large and medium ones run only where both output dimensions hold a
+// whole tile, so only the tiny one has a clamped-row (CLAMP) instantiation.
+constexpr int64_t kComputeUnits = 256;
 template <bool PS_ROW>
 static hipError_t run_gemm(GemmParams p, hipStream_t stream) {
   const int64_t large_tiles = (int64_t)((p.I + 255) / 256) * ((p.J + 255) / 256);
-  if (p.I >= 256 && p.J >= 256 && large_tiles >= 256)
+  if (p.I >= 256 && p.J >= 256 && large_tiles >= kComputeUnits) {
+    const int64_t medium_tiles = (int64_t)((p.I + 255) / 256) * ((p.J + 127) / 128);
+    const int64_t large_rounds = (large_tiles + kComputeUnits - 1) / kComputeUnits;
+    const int64_t medium_rounds = (medium_tiles + kComputeUnits - 1) / kComputeUnits;
+    if (54 * medium_rounds < 100 * large_rounds) return run_gemm_cfg<2, 4, 8, 2, PS_ROW, 3, false>(p, stream);
     return run_gemm_cfg<2, 4, 8, 4, PS_ROW, 2, false>(p, stream);
+  }
   const int64_t small_tiles = (int64_t)((p.I + 127) / 128) * ((p.J + 63) / 64);
   if (p.I >= 128 && p.J >= 64 && small_tiles >= 512) return run_gemm_cfg<2, 2, 4, 2, PS_ROW, 3, false>(p, stream);
   if (p.I >= 64 && p.J >= 64) return run_gemm_cfg<2, 2, 2, 2, PS_ROW, 3, false>(p, stream);

@@ -192,34 +192,40 @@ def test_exact_large_tiles_wgrad(grid):
                           448.0 ** 2 * (os1.astype(np.float64) @ os2.astype(np.float64).T))
 
 
-# Long contractions (K / 128 >= 64) put the large configuration on its
-# chip-wide tile order: whole 16 x 16 blocks of tiles shared by the eight XCDs,
-# the remaining partial rows and columns of tiles in the plain order. A 19 x 22
-# tile grid has one whole block plus both kinds of remainder (and a ragged last
-# tile along j); at least one output of every 256 x 256 tile is checked against
-# the oracle, so a tile computed in the wrong place or not at all would show.
+# Long contractions (K / 128 >= 64) put the large and medium configurations on
+# their chip-wide tile order: whole 16 x 16 blocks of tiles shared by the eight
+# XCDs, the remaining partial rows and columns of tiles in the plain order. The
+# large case is a 19 x 22 grid of 256 x 256 tiles (418 tiles, two rounds of the
+# chip); the medium case a 19 x 28 grid of 256 x 128 tiles (266 large tiles
+# would take two rounds, 532 medium ones take three at about half the cost).
+# Both have one or two whole blocks plus both kinds of remainder and a ragged
+# last tile along j. At least one output of every tile (one sample per tile
+# extent in each dimension) is checked against the oracle, so a tile computed
+# in the wrong place or not at all would show.
 
-def _one_per_tile(n, seed, group=1):
-    """Indices with one `group`-wide unit inside every 256-wide band of [0, n), plus the last unit."""
+def _one_per_tile(n, seed, group=1, band=256):
+    """Indices with one `group`-wide unit inside every `band`-wide band of [0, n), plus the last unit."""
     rng = np.random.default_rng(seed)
     units = []
-    for t in range((n + 255) // 256):
-        lo, hi = 256 * t // group, min(256 * t + 256, n) // group
+    for t in range((n + band - 1) // band):
+        lo, hi = band * t // group, min(band * t + band, n) // group
         units.append(int(rng.integers(lo, hi)))
     units = sorted(set(units) | {n // group - 1})
     return np.concatenate([np.arange(u * group, u * group + group) for u in units])
 
 
+@pytest.mark.parametrize("config,rows_j", [("large", 5504), ("medium", 3520)])
 @pytest.mark.parametrize("role", ["fwd", "dgrad", "wgrad"])
-def test_every_tile_long_contraction(role):
-    long_k, rows_j, cols_i = 8192, 5504, 4864      # 64 K blocks; 22 tiles along j, 19 along i
+def test_every_tile_long_contraction(role, config, rows_j):
+    long_k, cols_i = 8192, 4864                    # 64 K blocks; 19 tiles along i
+    jband = 256 if config == "large" else 128      # tile extent along the output rows
     if role == "fwd":
         M, N, K = rows_j, cols_i, long_k
     elif role == "dgrad":
         M, N, K = rows_j, long_k, cols_i
     else:
         M, N, K = long_k, rows_j, cols_i
-    note(f"every tile, long contraction: {role} M={M} N={N} K={K}")
+    note(f"every tile, long contraction ({config} tiles): {role} M={M} N={N} K={K}")
     x = inputs.bf16_normal_device((M, K), 1.0, 0.01, seed=71)
     w = inputs.bf16_normal_device((N, K), 0.02, 0.0, seed=72)
     dy = inputs.bf16_normal_device((M, N), 1e-3, 0.0, seed=73)
@@ -228,7 +234,7 @@ def test_every_tile_long_contraction(role):
         wq, ws, _ = fq.quantize_weight_128x128(w, transposed=False)
         out = fq.fp8_gemm_fwd(xq, xs, wq, ws)
         torch.cuda.synchronize()
-        r, c = _one_per_tile(M, 1), _one_per_tile(N, 2, group=128)
+        r, c = _one_per_tile(M, 1, band=jband), _one_per_tile(N, 2, group=128)
         oxq, oxs = quant.quantize_act_1x128(host_bits(x[r]))
         owq, ows, _ = quant.quantize_weight_128x128(host_bits(w[c]))
         ref = gemm.gemm_fwd(oxq, oxs, owq, ows)
@@ -237,7 +243,7 @@ def test_every_tile_long_contraction(role):
         wq, ws, wq_t = fq.quantize_weight_128x128(w)
         out = fq.fp8_gemm_dgrad(dyq, dys, wq_t, ws)
         torch.cuda.synchronize()
-        r, c = _one_per_tile(M, 3), _one_per_tile(K, 4, group=128)
+        r, c = _one_per_tile(M, 3, band=jband), _one_per_tile(K, 4, group=128)
         odq, ods = quant.quantize_act_1x128(host_bits(dy[r]))
         owq, ows, _ = quant.quantize_weight_128x128(host_bits(w[:, c]))
         ref = gemm.gemm_dgrad(odq, ods, owq, ows)
@@ -246,11 +252,11 @@ def test_every_tile_long_contraction(role):
         xq_t, xs_t = fq.transpose_quantize_128x1(x)
         out = fq.fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t)
         torch.cuda.synchronize()
-        r, c = _one_per_tile(N, 5), _one_per_tile(K, 6)
+        r, c = _one_per_tile(N, 5, band=jband), _one_per_tile(K, 6)
         oq1, os1 = quant.transpose_quantize_128x1(host_bits(dy[:, r]))
         oq2, os2 = quant.transpose_quantize_128x1(host_bits(x[:, c]))
         ref = gemm.gemm_wgrad(oq1, os1, oq2, os2)
-    _assert_close(host_bits(out[r][:, c]), ref, f"{role} every tile, long contraction")
+    _assert_close(host_bits(out[r][:, c]), ref, f"{role} every tile, long contraction, {config} tiles")
 
 
 # ---------------------------------------------------------- grouped calls --
@@ -339,14 +345,16 @@ def test_identity_weight():
 def test_rows_identical_across_tile_configurations(role):
     # Every tile configuration reduces K in the same order, so a token's output
     # row does not depend on how many tokens share the call. With N = K = 4096:
-    # 4096 tokens run the 256x256 tiles, 1024 the 128x64 tiles, 256 and 64 the
-    # 64x64 tiles, 17 the 64x64 tiles with clamped rows.
-    M, N, K = 4096, 4096, 4096
-    note(f"{role}: rows of a {M}-token call vs 1024/256/64/17-token calls (every tile configuration)")
+    # 4352 tokens run the 256x128 tiles (272 large tiles would take two rounds
+    # of the chip, 544 medium ones take three at about half the cost each),
+    # 4096 the 256x256 tiles, 1024 the 128x64 tiles, 256 and 64 the 64x64
+    # tiles, 17 the 64x64 tiles with clamped rows.
+    M, N, K = 4352, 4096, 4096
+    note(f"{role}: rows of a {M}-token call vs 4096/1024/256/64/17-token calls (every tile configuration)")
     a, as_, b, bs = _quantized_problem(role, M, N, K, seed=77)
     f = getattr(fq, f"fp8_gemm_{role}")
     full = f(a, as_, b, bs)
-    parts = {rows: f(a[:rows].contiguous(), as_[:rows].contiguous(), b, bs) for rows in (1024, 256, 64, 17)}
+    parts = {rows: f(a[:rows].contiguous(), as_[:rows].contiguous(), b, bs) for rows in (4096, 1024, 256, 64, 17)}
     torch.cuda.synchronize()
     for rows, part in parts.items():
         assert torch.equal(part, full[:rows]), f"{role}: {rows} rows differ from the {M}-row call"
