@@ -553,10 +553,14 @@ static hipError_t run_gemm_cfg(GemmParams p, hipStream_t stream) {
 //         workgroups per compute unit): for problems with fewer large tiles
 //         than compute units (decode-sized M, small outputs), where it
 //         measured 1.1-2.5x faster; more workgroups and a deeper prefetch.
-//  tiny:  64 x 64 tile, 4 wavefronts of 32 x 32, 3 LDS stages: when even the
-//         small tiles are too few (under two per compute unit), e.g. the
-//         long-contraction linears at 256 tokens, where the extra workgroups
-//         measured 10-25 % faster than the small tile.
+//  tiny:  64 x 64 tile, 4 wavefronts of 32 x 32, 4 LDS stages (67 KB, two
+//         workgroups per compute unit): when even the small tiles are too few
+//         (under two per compute unit), e.g. decode and the long-contraction
+//         linears at 256 tokens, where the extra workgroups measured 10-25 %
+//         faster than the small tile. These shapes stream their weights with
+//         little reuse; the fourth stage keeps one more K step of copies in
+//         flight (with weights rotated past the last-level cache: 3-24 %
+//         faster than 3 stages on every decode and 256-token shape measured).
 //  medium: 256 x 128 tile, 8 wavefronts of 128 x 32, 3 LDS stages (148-156
 //         KB, one workgroup per compute unit): instead of the large tile when
 //         the large tiles end just past a whole round of the 256 compute
@@ -581,8 +585,8 @@ static hipError_t run_gemm(GemmParams p, hipStream_t stream) {
   }
   const int64_t small_tiles = (int64_t)((p.I + 127) / 128) * ((p.J + 63) / 64);
   if (p.I >= 128 && p.J >= 64 && small_tiles >= 512) return run_gemm_cfg<2, 2, 4, 2, PS_ROW, 3, false>(p, stream);
-  if (p.I >= 64 && p.J >= 64) return run_gemm_cfg<2, 2, 2, 2, PS_ROW, 3, false>(p, stream);
-  return run_gemm_cfg<2, 2, 2, 2, PS_ROW, 3, true>(p, stream);
+  if (p.I >= 64 && p.J >= 64) return run_gemm_cfg<2, 2, 2, 2, PS_ROW, 4, false>(p, stream);
+  return run_gemm_cfg<2, 2, 2, 2, PS_ROW, 4, true>(p, stream);
 }
 
 template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
