@@ -213,6 +213,29 @@ def test_dual_edge_groups():
     assert np.array_equal(host(qt), oqt)
 
 
+@pytest.mark.parametrize("shape", [(4224, 1152), (4200, 1144)])
+def test_dual_and_transpose_every_byte_past_256_workgroups(shape):
+    # 33 token blocks x 9 channel blocks = 297 workgroups: the first 256 are
+    # renumbered so each XCD takes 32 consecutive token blocks, the last 41
+    # keep their order; the second shape is ragged in both dimensions (the
+    # TAIL instantiation). Every code and scale byte is compared.
+    M, C = shape
+    note(f"dual and transpose_128x1, every byte, {M}x{C}")
+    x = _np_bf16(M, C, seed=M + C)
+    xd = dev_bf16(x)
+    xq, xs, qt, st = fq.quantize_dual_1x128_128x1(xd)
+    qt2, st2 = fq.transpose_quantize_128x1(xd)
+    torch.cuda.synchronize()
+    oq, os_ = quant.quantize_act_1x128(x)
+    oqt, ost = quant.transpose_quantize_128x1(x)
+    assert_bytes_equal(host(xq), oq, "dual xq")
+    assert_bytes_equal(host(xs), os_, "dual xs")
+    assert_bytes_equal(host(qt), oqt, "dual xq_t")
+    assert_bytes_equal(host(st), ost, "dual xs_t")
+    assert_bytes_equal(host(qt2), oqt, "transpose xq_t")
+    assert_bytes_equal(host(st2), ost, "transpose xs_t")
+
+
 def test_dual_full_size_equals_single_output_kernels():
     M, C = 32768, 27648
     note(f"dual full size [{M},{C}] vs the single-output kernels (all bytes) and the oracle (sampled)")
