@@ -493,9 +493,13 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
       const int jr = lane / CHUNKS + ROWS_PER_PASS * k;
       const u32x4 v = *reinterpret_cast<const u32x4*>(eb + jr * ROWB + ((c ^ (jr & (CHUNKS - 1))) * 16));
       const int j = j0 + wj * C::WJ + jr;
-      // Iout is a multiple of 8, so each 16-byte chunk is stored whole or not at all
+      // Iout is a multiple of 8, so each 16-byte chunk is stored whole or not
+      // at all. Non-temporal: the output is not read again by this kernel, and
+      // keeping it out of L2 leaves room for the operand bands that other
+      // tiles still read (1-2.5 % faster on the large GEMMs, 7-9 % on a
+      // 256-token grouped WGrad, whose time is its output).
       if ((!CLAMP || j < p.J) && i < p.Iout)
-        *reinterpret_cast<u32x4*>(p.out + (int64_t)j * p.ldo + i) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p.out + (int64_t)j * p.ldo + i));
     }
   }
 #endif
