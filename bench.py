@@ -41,7 +41,13 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s (fwd/DGrad/WGrad), % of FP8 MFMA peak"
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA, published
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "qwen25_32b_linears_m32768"
+RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # 625 FLOP per byte: MFMA- vs HBM-bound
 ROTATE_BYTES = 640 << 20        # > 256 MB last-level cache + 8 x 4 MB L2, with margin
+
+
+def attainable_tflops(flop_per_byte):
+    """Roofline: min(FP8 MFMA peak, arithmetic intensity x HBM peak), TFLOP/s."""
+    return min(PEAK_FP8_TFLOPS, flop_per_byte * PEAK_HBM_GBS / 1e3)
 MAX_SETS = 32
 
 
@@ -319,7 +325,11 @@ def summarize_runs(paths):
         for key, k in r["kernels"].items():
             if "tflops" in k:
                 gbs = f", {k['gbs']} GB/s ({100 * k['gbs'] / PEAK_HBM_GBS:.1f} % HBM)" if "gbs" in k else ""
-                print(f"| {key} | {k['ms']} | {k['tflops']} TFLOP/s{gbs} | {100 * k['frac_fp8_peak']:.1f} % FP8 |")
+                if k.get("bound") == "hbm":
+                    roof = f"{100 * k['gbs'] / PEAK_HBM_GBS:.1f} % HBM (HBM-bound, {k['flop_per_byte']} FLOP/B)"
+                else:
+                    roof = f"{100 * k['frac_fp8_peak']:.1f} % FP8"
+                print(f"| {key} | {k['ms']} | {k['tflops']} TFLOP/s{gbs} | {roof} |")
             else:
                 print(f"| {key} | {k['ms']} | {k['gbs']} GB/s | {100 * k['frac_hbm_peak']:.1f} % HBM |")
         print()
@@ -475,19 +485,31 @@ def main():
     for p in per:
         if p["flops"]:
             tf = p["flops"] / (p["ms"] * 1e-3) / 1e12
+            ai = p["flops"] / p["bytes"]
             kernels[p["key"]] = {"ms": round(p["ms"], 4), "tflops": round(tf, 1),
                                  "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
-                                 "gbs": round(p["bytes"] / (p["ms"] * 1e-3) / 1e9, 1)}
+                                 "gbs": round(p["bytes"] / (p["ms"] * 1e-3) / 1e9, 1),
+                                 "flop_per_byte": round(ai, 1),
+                                 "bound": "mfma" if ai >= RIDGE else "hbm",
+                                 "frac_attainable": round(tf / attainable_tflops(ai), 4)}
         else:
             gbs = p["bytes"] / (p["ms"] * 1e-3) / 1e9
             kernels[p["key"]] = {"ms": round(p["ms"], 4), "gbs": round(gbs, 1),
                                  "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
     dom = dict(per[dom_i], ms=dom_ms)       # the dominant launch, timed inside the timed region
-    if dom["flops"]:
+    if dom["flops"] and dom["flops"] / dom["bytes"] >= RIDGE:
         achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_FP8_TFLOPS, 4)}
+    elif dom["flops"]:
+        # A GEMM below the ridge point (decode, a few hundred tokens) is bound by
+        # HBM: its algorithmic bytes over the time, against the HBM peak.
+        achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "flop_per_byte": round(dom["flops"] / dom["bytes"], 1),
+                "tflops": round(dom["flops"] / (dom["ms"] * 1e-3) / 1e12, 1)}
     else:
         achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
