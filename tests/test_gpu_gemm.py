@@ -360,6 +360,26 @@ def test_rows_identical_across_tile_configurations(role):
         assert torch.equal(part, full[:rows]), f"{role}: {rows} rows differ from the {M}-row call"
 
 
+@pytest.mark.parametrize("role", ["fwd", "dgrad"])
+def test_rows_identical_wide_weight_few_tokens(role):
+    # 256 tokens against 27648 weight rows run the 256x128 tiles (216 of them,
+    # one round of the chip); 1024 tokens the 256x256 tiles, 64 and 17 the
+    # 64x64 tiles. A token's row is the same bits in every one.
+    M, N, K = 256, 27648, 1024
+    if role == "dgrad":
+        N, K = 1024, 27648
+    note(f"{role}: rows of a {M}-token call vs 1024/64/17-token calls, 27648 weight rows")
+    a_full, as_full, b, bs = _quantized_problem(role, 1024, N, K, seed=78)
+    f = getattr(fq, f"fp8_gemm_{role}")
+    big = f(a_full, as_full, b, bs)
+    full = f(a_full[:M].contiguous(), as_full[:M].contiguous(), b, bs)
+    parts = {rows: f(a_full[:rows].contiguous(), as_full[:rows].contiguous(), b, bs) for rows in (64, 17)}
+    torch.cuda.synchronize()
+    assert torch.equal(full, big[:M]), f"{role}: the {M}-row call differs from the 1024-row call"
+    for rows, part in parts.items():
+        assert torch.equal(part, full[:rows]), f"{role}: {rows} rows differ from the {M}-row call"
+
+
 def test_gemm_determinism():
     note("GEMMs: repeated calls give identical bytes")
     x = inputs.bf16_normal_device((2048, 4096), 1.0, 0.01, seed=21)
