@@ -28,11 +28,11 @@
 // uniform over the wavefront.
 //
 // Tiles: a workgroup owns a BI x BJ output tile and walks K in 128-byte steps.
-// Both operand tiles of a step are staged in LDS (two or three stages) with
+// Both operand tiles of a step are staged in LDS (two to four stages) with
 // their 16-byte chunks XOR-swizzled by row so that the MFMA fragment reads are
 // free of bank conflicts. Workgroups are mapped to tiles so that each XCD works on
 // a compact band of the output (its own L2), in groups along i; for long
-// contractions the large configuration also keeps the eight XCDs inside one
+// contractions the 8-wavefront configurations also keep the eight XCDs inside one
 // 16 x 16 block of tiles at a time (shared operand bands in the last-level
 // cache).
 #include "device_common.h"
@@ -76,9 +76,9 @@ __device__ __forceinline__ void map_tile(int bid, int nblk, int tiles_i, int til
   tj = in_group / gsize;
 }
 
-// Chip-wide tile order for long contractions, used by the large tile
-// configuration (one workgroup per compute unit, so 256 workgroups run at
-// once). The output is cut into supertiles of 16 x 16 tiles; the 256
+// Chip-wide tile order for long contractions, used by the large and medium
+// tile configurations (8 wavefronts, one workgroup per compute unit, so 256
+// workgroups run at once). The output is cut into supertiles of 16 x 16 tiles; the 256
 // workgroups of one round of the chip share a supertile, XCD x taking the
 // 4 (i) x 8 (j) block at (4 (x % 4), 8 (x / 4)) of it. Each XCD still works
 // on a compact block (12 operand bands for 32 tiles in its L2), and the eight
