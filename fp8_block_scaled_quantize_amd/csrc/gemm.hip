@@ -608,6 +608,12 @@ static hipError_t run_grouped_cfg(const GemmParams* probs, int count, hipStream_
   using C = GemmCfg<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST>;
   GroupedParams gp{};
   gp.count = count;
+  // Each problem's block range starts at a multiple of the XCD count; with
+  // 8 wavefronts (one workgroup per compute unit) at a multiple of 256, so
+  // that a problem's chip-wide 16 x 16 supertiles line up with the rounds of
+  // 256 workgroups the chip runs at once (grouped WGrad of the 32B linears at
+  // 32768 tokens: 12.07 -> 11.99 ms; the padding blocks exit at once).
+  constexpr int ALIGN = C::NT == 512 ? 256 : NUM_XCD;
   int total = 0;
   for (int g = 0; g < count; ++g) {
     GemmParams q = probs[g];
@@ -615,7 +621,7 @@ static hipError_t run_grouped_cfg(const GemmParams* probs, int count, hipStream_
     q.tiles_j = (q.J + C::BJ - 1) / C::BJ;
     gp.prob[g] = q;
     gp.start[g] = total;
-    total += (q.tiles_i * q.tiles_j + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+    total += (q.tiles_i * q.tiles_j + ALIGN - 1) / ALIGN * ALIGN;
   }
   gp.start[count] = total;
   hipLaunchKernelGGL((fp8_gemm_grouped_kernel<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP>), dim3(total),
