@@ -80,12 +80,3 @@ def bf16_bits_to_f32(bits):
     """bf16 bit patterns (uint16) -> float32, exactly (a 16-bit left shift)."""
     b = np.asarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32)
-
-
-def f32_to_bf16_bits_exact(values):
-    """float32 values that are exactly bf16 -> their bf16 bit patterns."""
-    v = np.asarray(values, dtype=np.float32)
-    u = v.view(np.uint32)
-    if np.any(u & 0xFFFF):
-        raise ValueError("value is not exactly representable in bf16")
-    return (u >> 16).astype(np.uint16)

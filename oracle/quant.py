@@ -38,27 +38,11 @@ GROUP = 128
 FP8_MAX = np.float32(448.0)
 
 
-def quantize_group(values_f32):
-    """Quantize one group (any shape) of float32 values that came from bf16.
-
-    Returns (codes uint8 of the same shape, scale as np.float32).
-    """
-    x = np.asarray(values_f32, dtype=np.float32)
-    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
-    if amax == 0:
-        s = np.float32(1.0)
-    else:
-        s = np.float32(amax / FP8_MAX)           # float32 / float32 -> float32
-    q = encode(np.float32(x / s))                # float32 division, then RNE
-    return q, s
-
-
 def _grouped_scales_and_codes(groups):
-    """Apply quantize_group to every row of a [G, n] array (vectorised form).
-
-    Identical to calling quantize_group on each row: the amax is per row, the
-    scale is one float32 division per row, the quotient one float32 division
-    per element.
+    """Quantize every row of a [G, n] float32 array as one group (the rule in
+    the module docstring): the amax is per row, the scale is one float32
+    division per row (1.0 for an all-zero row), the quotient one float32
+    division per element, then the E4M3 encoder.
     """
     g = np.asarray(groups, dtype=np.float32)
     amax = np.max(np.abs(g), axis=1)
