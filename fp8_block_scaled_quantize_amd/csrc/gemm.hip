@@ -37,6 +37,7 @@
 // cache).
 #include "device_common.h"
 #include "launch.h"
+#include "tile_map.h"
 
 #include <type_traits>
 
@@ -55,64 +56,6 @@ struct GemmParams {
   int ps_ib, ps_kb;  // block P scale of (i, kb) at Ps[(i / 128) * ps_ib + kb * ps_kb]
   int tiles_i, tiles_j;
 };
-
-// XCD-aware tile order. The hardware hands out workgroup ids round-robin over
-// the 8 XCDs; ids b, b+8, b+16, ... share an XCD. Renumber so that each XCD
-// gets a contiguous range of logical tiles, then walk logical tiles in groups
-// of GROUP_I tiles along i (all j for one group before the next group).
-constexpr int NUM_XCD = 8;
-constexpr int GROUP_I = 8;
-
-__device__ __forceinline__ void map_tile(int bid, int nblk, int tiles_i, int tiles_j, int& ti, int& tj) {
-  const int xcd = bid % NUM_XCD, k = bid / NUM_XCD;
-  const int per = nblk / NUM_XCD, rem = nblk % NUM_XCD;
-  const int logical = xcd * per + (xcd < rem ? xcd : rem) + k;
-  const int group_span = GROUP_I * tiles_j;
-  const int group = logical / group_span;
-  const int first_i = group * GROUP_I;
-  const int gsize = (tiles_i - first_i) < GROUP_I ? (tiles_i - first_i) : GROUP_I;
-  const int in_group = logical - group * group_span;
-  ti = first_i + in_group % gsize;
-  tj = in_group / gsize;
-}
-
-// Chip-wide tile order for long contractions, used by the large and medium
-// tile configurations (8 wavefronts, one workgroup per compute unit, so 256
-// workgroups run at once). The output is cut into supertiles of 16 x 16 tiles; the 256
-// workgroups of one round of the chip share a supertile, XCD x taking the
-// 4 (i) x 8 (j) block at (4 (x % 4), 8 (x / 4)) of it. Each XCD still works
-// on a compact block (12 operand bands for 32 tiles in its L2), and the eight
-// XCDs fetch only the supertile's 32 bands between them, the repeats served
-// by the last-level cache instead of HBM. Supertiles are walked along j.
-// Tiles outside the whole supertiles (a last partial row or column of them)
-// take map_tile's order on their own rectangles. Measured on the linears of a
-// 32B-parameter model at 32768 tokens: 3-4 % faster where K / 128 >= 64
-// (long-contraction DGrad and WGrad), 0.5-1 % slower at K = 5120.
-__device__ __forceinline__ void map_tile_super(int bid, int nblk, int tiles_i, int tiles_j, int& ti, int& tj) {
-  const int si = tiles_i / 16, sj = tiles_j / 16;
-  const int nsup = si * sj;
-  if (bid < 256 * nsup) {
-    const int xcd = bid % NUM_XCD, k = bid / NUM_XCD;
-    const int st = k / 32, s = k % 32;
-    ti = (st / sj) * 16 + 4 * (xcd % 4) + (s % 4);
-    tj = (st % sj) * 16 + 8 * (xcd / 4) + (s / 4);
-    return;
-  }
-  // bid - 256 nsup has the XCD of bid (256 nsup is a multiple of 8), and so
-  // has the offset into the second rectangle (its start 16 si rj is too).
-  int r = bid - 256 * nsup;
-  const int rj = tiles_j - 16 * sj, ri = tiles_i - 16 * si;
-  const int na = 16 * si * rj;    // i < 16 si, j >= 16 sj
-  if (r < na) {
-    map_tile(r, na, 16 * si, rj, ti, tj);
-    tj += 16 * sj;
-  } else {                        // i >= 16 si, every j
-    r -= na;
-    map_tile(r, ri * tiles_j, ri, tiles_j, ti, tj);
-    ti += 16 * si;
-  }
-}
-constexpr int SUPERTILE_MIN_KB = 64;
 
 template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST_ = 2>
 struct GemmCfg {
@@ -524,8 +467,7 @@ struct GroupedParams {
 template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
 __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_grouped_kernel(GroupedParams gp) {
   const int bid = (int)blockIdx.x;
-  int g = 0;
-  while (g + 1 < gp.count && bid >= gp.start[g + 1]) ++g;   // uniform over the workgroup
+  const int g = grouped_problem(bid, gp.start, gp.count);   // uniform over the workgroup
   const GemmParams& p = gp.prob[g];
   const int nblk = p.tiles_i * p.tiles_j;
   const int local = bid - gp.start[g];
@@ -614,16 +556,15 @@ static hipError_t run_grouped_cfg(const GemmParams* probs, int count, hipStream_
   // 256 workgroups the chip runs at once (grouped WGrad of the 32B linears at
   // 32768 tokens: 12.07 -> 11.99 ms; the padding blocks exit at once).
   constexpr int ALIGN = C::NT == 512 ? 256 : NUM_XCD;
-  int total = 0;
+  int tiles[kMaxGroup];
   for (int g = 0; g < count; ++g) {
     GemmParams q = probs[g];
     q.tiles_i = (q.I + C::BI - 1) / C::BI;
     q.tiles_j = (q.J + C::BJ - 1) / C::BJ;
     gp.prob[g] = q;
-    gp.start[g] = total;
-    total += (q.tiles_i * q.tiles_j + ALIGN - 1) / ALIGN * ALIGN;
+    tiles[g] = q.tiles_i * q.tiles_j;
   }
-  gp.start[count] = total;
+  const int total = grouped_layout(tiles, count, ALIGN, gp.start);
   hipLaunchKernelGGL((fp8_gemm_grouped_kernel<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP>), dim3(total),
                      dim3(C::NT), 0, stream, gp);
   return hipGetLastError();

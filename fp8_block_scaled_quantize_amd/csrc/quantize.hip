@@ -19,6 +19,7 @@
 // run the instantiation without the masks.
 #include "device_common.h"
 #include "launch.h"
+#include "tile_map.h"
 
 namespace fp8bsq {
 
@@ -242,27 +243,12 @@ constexpr int T_THREADS = 256;
 constexpr int T_CH = 128;
 constexpr int T_ROW_BYTES = 128 + 8;  // padded LDS row of the transposed code tile
 
-// Workgroup order of the 128x1 and dual kernels (grid [token blocks,
-// channel blocks]). The hardware deals workgroup ids round-robin over the 8
-// XCDs; here each run of 256 ids is renumbered so that every XCD takes 32
-// consecutive token blocks of one channel block, one after another. The 4-byte
-// scale stores of those 32 workgroups then land in the same 128-byte lines of
-// the transposed scales (32 consecutive token blocks of one channel) and, one
-// run later, beside each other in the row scales, while the lines are still in
-// that XCD's L2, so the lines go out to HBM merged instead of as dozens of
-// partial writes (5-9 % faster, same bytes). Ids past the last whole run of
-// 256 keep their order. Every tensor has fewer than 2^40 elements and a
-// workgroup covers 2^14, so the ids fit in int.
+// Workgroup order of the 128x1 and dual kernels (grid [token blocks, channel
+// blocks]): token_major_block_of in tile_map.h. Every tensor has fewer than
+// 2^40 elements and a workgroup covers 2^14, so the ids fit in int.
 __device__ __forceinline__ void token_major_block(int& mb, int& cbi) {
   const int nx = (int)gridDim.x, n = nx * (int)gridDim.y;
-  const int bid = (int)blockIdx.x + (int)blockIdx.y * nx;
-  int L = bid;
-  if (bid < (n / 256) * 256) {
-    const int xcd = bid % 8, k = bid / 8;
-    L = (k / 32) * 256 + xcd * 32 + (k % 32);
-  }
-  mb = L % nx;
-  cbi = L / nx;
+  token_major_block_of((int)blockIdx.x + (int)blockIdx.y * nx, nx, n, mb, cbi);
 }
 
 template <bool TAIL>
