@@ -4,7 +4,9 @@
 
 Compiles every csrc/*.hip to an object file, then links one shared library
 next to this file; also builds the stand-alone GPU check programs under
-tests/gpu (each tests/gpu/<name>.hip -> tests/gpu/<name>), which GPU tests run.
+tests/gpu (each tests/gpu/<name>.hip -> tests/gpu/<name>), which GPU tests run,
+and the ceilings micro-benchmark bench_ceilings.hip -> bench_ceilings at the
+repository root, which bench.py runs.
 Flags:
   --offload-arch=gfx950                  MI355X only
   -O3 -std=c++17 -fPIC
@@ -44,12 +46,20 @@ COMMON_FLAGS = [
 CHECKS_DIR = os.path.join(ROOT, "tests", "gpu")
 
 
+CEILINGS_SRC = os.path.join(ROOT, "bench_ceilings.hip")
+CEILINGS_EXE = os.path.join(ROOT, "bench_ceilings")
+
+
 def check_programs():
-    """(source, executable) pairs of the HIP check programs under tests/gpu."""
-    if not os.path.isdir(CHECKS_DIR):
-        return []
-    return [(os.path.join(CHECKS_DIR, f), os.path.join(CHECKS_DIR, f[:-4]))
-            for f in sorted(os.listdir(CHECKS_DIR)) if f.endswith(".hip")]
+    """(source, executable) pairs of the stand-alone HIP programs: the GPU
+    checks under tests/gpu and the ceilings micro-benchmark."""
+    progs = []
+    if os.path.isdir(CHECKS_DIR):
+        progs = [(os.path.join(CHECKS_DIR, f), os.path.join(CHECKS_DIR, f[:-4]))
+                 for f in sorted(os.listdir(CHECKS_DIR)) if f.endswith(".hip")]
+    if os.path.exists(CEILINGS_SRC):
+        progs.append((CEILINGS_SRC, CEILINGS_EXE))
+    return progs
 
 
 def sources():
