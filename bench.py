@@ -84,7 +84,41 @@ def parse():
                     help="print a markdown table of the launches of bench.py result lines (files)")
     ap.add_argument("--summarize-counters", metavar="CSV", nargs="+", default=None,
                     help="host only: per (kernel, grid) averages of rocprofv3 --pmc counter CSVs")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured-ceilings micro-benchmark (bench_ceilings) run before the step")
     return ap.parse_args()
+
+
+CEILINGS_EXE = os.path.join(ROOT, "bench_ceilings")
+
+
+def measured_ceilings():
+    """Run the ceilings micro-benchmark (a separate process, before this one
+    touches the GPU) and return its streams and MFMA loops by name."""
+    import subprocess
+    if not os.path.exists(CEILINGS_EXE):
+        return None
+    r = subprocess.run([CEILINGS_EXE], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=120)
+    if r.returncode != 0:
+        print(f"[bench] bench_ceilings failed: {r.stdout[-500:]}", file=sys.stderr, flush=True)
+        return None
+    out = {"streams": {}, "mfma_loops": {}}
+    for line in r.stdout.splitlines():
+        d = json.loads(line)
+        if "stream" in d:
+            out["streams"][d.pop("stream")] = d
+        elif "loop" in d:
+            out["mfma_loops"][d.pop("loop")] = d
+        elif "device" in d:
+            out["device"] = d["device"]
+    return out
+
+
+# The measured stream whose read/write mix matches each quantizer kind:
+# 2 B read + 1 B written per element (1x128, 128x1, 128x128 without the
+# transposed copy) or 2 B read + 2 B written (dual, 128x128 with it).
+STREAM_FOR = {"quant_act": "read2_write1", "quant_transpose": "read2_write1", "quant_dual": "copy_nt",
+              "quant_weight": "copy_nt", "quant_weight_nt": "read2_write1"}
 
 
 def act_bytes(rows, cols):
@@ -140,7 +174,8 @@ class Linear:
         fwd, dgrad, wgrad = ("fwd" in self.passes), ("dgrad" in self.passes), ("wgrad" in self.passes)
         x_dual, dy_dual = self.dual and fwd and wgrad, self.dual and dgrad and wgrad
         L = []
-        L.append(("quant_weight", f"{self.name}.w[{N},{K}]", 0, weight_bytes(N, K, self.wq_t is not None),
+        L.append(("quant_weight" if self.wq_t is not None else "quant_weight_nt", f"{self.name}.w[{N},{K}]", 0,
+                  weight_bytes(N, K, self.wq_t is not None),
                   lambda: fq.quantize_weight_128x128(self.w, self.wq_t is not None, self.wq, self.ws, self.wq_t)))
         if x_dual:
             L.append(("quant_dual", f"{self.name}.x_dual[{M},{K}]", 0, dual_bytes(M, K),
@@ -249,9 +284,12 @@ def cpu_baseline(inputs, wl, tokens=16384):
     gemm.gemm_wgrad(dyq_t, dys_t, xq_t, xs_t)
     dt = time.perf_counter() - t0
     flops = 3 * 2 * M * N * K
+    import hashlib
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{lin['name']} linear ({K}->{N}) at {M} tokens: all five quantizations and "
-                      f"fwd/dgrad/wgrad in fp64, {dt:.1f} s wall",
+                      f"fwd/dgrad/wgrad in fp64, {dt:.1f} s wall; inputs drawn on the host (numpy PCG64, "
+                      f"seed 0, the same recipe as the step's), not the step's device-drawn tensors",
+            "inputs_sha256": {k: hashlib.sha256(t[k].tobytes()).hexdigest()[:16] for k in ("x", "w", "dy")},
             "seconds": dt}
 
 
@@ -351,6 +389,8 @@ def main():
               "is not measured here.", file=sys.stderr)
         sys.exit(2)
 
+    ceilings = None if args.no_ceilings else measured_ceilings()
+
     import torch
     import fp8_block_scaled_quantize_amd as fq
     from fp8_block_scaled_quantize_amd import inputs
@@ -371,9 +411,9 @@ def main():
             layer.defer_wgrad = grouped
         steps = [l for layer in layers for l in layer.launches()]
         if args.weights_prequantized:
-            for l in [l for l in steps if l[0] == "quant_weight"]:
+            for l in [l for l in steps if l[0].startswith("quant_weight")]:
                 l[4]()
-            steps = [l for l in steps if l[0] != "quant_weight"]
+            steps = [l for l in steps if not l[0].startswith("quant_weight")]
         if grouped:
             # the WGrads of all linears in one launch (they are independent of the
             # rest of the step; a backward pass can defer them to the end)
@@ -496,6 +536,11 @@ def main():
             gbs = p["bytes"] / (p["ms"] * 1e-3) / 1e9
             kernels[p["key"]] = {"ms": round(p["ms"], 4), "gbs": round(gbs, 1),
                                  "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+            kind = p["kind"]
+            if ceilings and STREAM_FOR.get(kind) in ceilings["streams"]:
+                name = STREAM_FOR[kind]
+                kernels[p["key"]]["frac_stream_ceiling"] = round(gbs / ceilings["streams"][name]["gbs"], 4)
+                kernels[p["key"]]["stream_ceiling"] = name
 
     dom = dict(per[dom_i], ms=dom_ms)       # the dominant launch, timed inside the timed region
     if dom["flops"] and dom["flops"] / dom["bytes"] >= RIDGE:
@@ -549,6 +594,8 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    if ceilings:
+        result["ceilings"] = ceilings
     if not args.no_producers:
         prod = time_producers(fq, inputs, torch, wl)
         if prod:

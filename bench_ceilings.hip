@@ -1,0 +1,416 @@
+// Measured ceilings of the MI355X for the two roofs the FP8 linear-layer
+// kernels sit under: streaming HBM bandwidth (the quantizers, the weight-
+// streaming GEMMs) and the FP8 matrix-core rate with the instruction mix of
+// the block-scaled GEMM (Resumen Técnico: Jet-RL, "Esquema de Cuantización":
+// FP8 GEMMs whose operands carry one scale per 128-long block, so each block's
+// partial sum is promoted into an fp32 accumulator).
+//
+// Streams (2 GiB buffers, far past the 256 MB last-level cache; bytes counted
+// as read + written; each is timed over a sweep of grid sizes and vectors in
+// flight per lane and the best is reported):
+//   copy        16-byte loads and stores, 1 B written per byte read
+//   copy_nt     the same with non-temporal loads and stores (the quantizers'
+//               cache hints)
+//   read        16-byte non-temporal loads only (a running XOR keeps them live)
+//   write       16-byte non-temporal stores only
+//   read2_write1  16-byte loads, 8-byte stores: the 1x128 quantizer's 2 B in,
+//               1 B out per element
+//   kmajor_SEG  a [28672, 4096] byte matrix (a decode weight) read by 448
+//               workgroups of 64 rows, SEG bytes of each row per step (the
+//               GEMM's K-block order is SEG = 128)
+// MFMA loops (8 wavefronts per compute unit, 2 per SIMD, operands in
+// registers, each wavefront a 128 x 64 tile = 8 x 4 MFMAs per K block, as the
+// GEMM's large tile):
+//   mfma        v_mfma_f32_16x16x128_f8f6f4 only, chained through the
+//               accumulator input
+//   mfma_fma4   each MFMA with a zero accumulator, its 4-element partial
+//               promoted by 4 FMAs (forward / DGrad: one block scale)
+//   mfma_valu8  promoted by 4 multiplies + 4 FMAs (WGrad: two per-row scales)
+//   mfma_lds    mfma_fma4 with every fragment read from a swizzled LDS tile
+//               each K block (P fragments two slices ahead, Q at the block
+//               start), no global copies and no barrier
+// Rates are against 5.0 PFLOP/s dense FP8 (2 x 16 x 16 x 128 FLOP per MFMA)
+// and 8 TB/s HBM.
+//
+// Output: one JSON object per line. Exit status 0 when everything ran.
+// Build (done by the package build): hipcc --offload-arch=gfx950 -O3 <this> -o bench_ceilings
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#define CHECK(call)                                                               \
+  do {                                                                            \
+    hipError_t e_ = (call);                                                       \
+    if (e_ != hipSuccess) {                                                       \
+      printf("HIP error %s at %s:%d\n", hipGetErrorString(e_), __FILE__, __LINE__); \
+      return 2;                                                                   \
+    }                                                                             \
+  } while (0)
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ streams --
+constexpr int S_THREADS = 256;
+
+// Each lane moves U 16-byte vectors per trip (all loads issued before any
+// store), trips strided by the whole grid; n is a multiple of U * grid size.
+template <bool NT, int U>
+__global__ __launch_bounds__(S_THREADS) void k_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n) {
+  const size_t lanes = (size_t)gridDim.x * S_THREADS;
+  for (size_t i = (size_t)blockIdx.x * S_THREADS + threadIdx.x; i < n; i += U * lanes) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = NT ? __builtin_nontemporal_load(src + i + u * lanes) : src[i + u * lanes];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (NT) __builtin_nontemporal_store(v[u], dst + i + u * lanes);
+      else dst[i + u * lanes] = v[u];
+    }
+  }
+}
+
+template <int U>
+__global__ __launch_bounds__(S_THREADS) void k_read(const u32x4* __restrict__ src, uint32_t* __restrict__ sink, size_t n) {
+  const size_t lanes = (size_t)gridDim.x * S_THREADS;
+  uint32_t x = 0;
+  for (size_t i = (size_t)blockIdx.x * S_THREADS + threadIdx.x; i < n; i += U * lanes) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * lanes);
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  sink[(size_t)blockIdx.x * S_THREADS + threadIdx.x] = x;
+}
+
+template <int U>
+__global__ __launch_bounds__(S_THREADS) void k_write(u32x4* __restrict__ dst, size_t n) {
+  const size_t lanes = (size_t)gridDim.x * S_THREADS;
+  for (size_t i = (size_t)blockIdx.x * S_THREADS + threadIdx.x; i < n; i += U * lanes) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(u32x4{(uint32_t)i, 1u, 2u, (uint32_t)u}, dst + i + u * lanes);
+  }
+}
+
+// n 16-byte loads, n 8-byte stores
+template <int U>
+__global__ __launch_bounds__(S_THREADS) void k_read2_write1(const u32x4* __restrict__ src, u32x2* __restrict__ dst,
+                                                           size_t n) {
+  const size_t lanes = (size_t)gridDim.x * S_THREADS;
+  for (size_t i = (size_t)blockIdx.x * S_THREADS + threadIdx.x; i < n; i += U * lanes) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * lanes);
+#pragma unroll
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(u32x2{v[u][0] ^ v[u][1], v[u][2] ^ v[u][3]}, dst + i + u * lanes);
+  }
+}
+
+// The weight-streaming GEMMs' read order: a row-major [R, C] byte matrix
+// read by workgroups that each own 64 rows and walk the columns in steps of
+// SEG bytes (each step one SEG-byte segment of each of the 64 rows), as a
+// GEMM reads its weight operand K block by K block. Each lane loads 16 bytes;
+// four steps are in flight per lane.
+template <int SEG>
+__global__ __launch_bounds__(S_THREADS) void k_read_kmajor(const uint8_t* __restrict__ src, uint32_t* __restrict__ sink,
+                                                           int C) {  // src: this call's matrix
+  constexpr int LANES_PER_ROW = SEG / 16;                 // lanes covering one row segment
+  constexpr int ROWS_PER_PASS = S_THREADS / LANES_PER_ROW;
+  const int t = threadIdx.x;
+  const uint8_t* base = src + (size_t)blockIdx.x * 64 * C;
+  uint32_t x = 0;
+  for (int c0 = 0; c0 < C; c0 += 4 * SEG) {
+#pragma unroll
+    for (int r0 = 0; r0 < 64; r0 += ROWS_PER_PASS) {
+      const int row = r0 + t / LANES_PER_ROW;
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)row * C + c0 + u * SEG +
+                                                                         (t % LANES_PER_ROW) * 16));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+  }
+  sink[(size_t)blockIdx.x * S_THREADS + t] = x;
+}
+
+// -------------------------------------------------------------- MFMA loops --
+constexpr int M_THREADS = 512;   // 8 wavefronts: 2 per SIMD
+constexpr int SI = 8, SJ = 4;    // a wavefront's 128 x 64 tile in 16 x 16 MFMA tiles
+
+__device__ __forceinline__ f32x4 mfma(const i32x8& a, const i32x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Operands derived from `seed` so nothing folds; results summed into out[tid].
+__device__ __forceinline__ i32x8 frag(const int* seed, int k) {
+  const int s = seed[k & 63];
+  return i32x8{s, s ^ 0x01010101, s ^ 0x02020202, s ^ 0x04040404, s ^ 0x08080808, s ^ 0x10101010,
+               s ^ 0x20202020, s ^ 0x00030303};
+}
+
+// MODE 0: MFMA chained through the accumulator; 1: + 4 FMA promotion;
+// 2: + 4 multiplies and 4 FMAs.
+template <int MODE>
+__global__ __launch_bounds__(M_THREADS) void k_mfma(const int* __restrict__ seed, const float* __restrict__ scales,
+                                                    float* __restrict__ out, int iters) {
+  const int lane = threadIdx.x & 63;
+  i32x8 p[SI], q[SJ];
+#pragma unroll
+  for (int a = 0; a < SI; ++a) p[a] = frag(seed, lane + a);
+#pragma unroll
+  for (int b = 0; b < SJ; ++b) q[b] = frag(seed, lane + 17 * b + 3);
+  const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 acc[SI][SJ];
+#pragma unroll
+  for (int a = 0; a < SI; ++a)
+#pragma unroll
+    for (int b = 0; b < SJ; ++b) acc[a][b] = zero;
+  float cs[SJ];
+  f32x4 rs = {scales[lane & 7], scales[(lane + 1) & 7], scales[(lane + 2) & 7], scales[(lane + 3) & 7]};
+#pragma unroll
+  for (int b = 0; b < SJ; ++b) cs[b] = scales[(lane + b) & 7];
+  f32x4 dprev[SJ];
+#pragma unroll
+  for (int b = 0; b < SJ; ++b) dprev[b] = zero;
+
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int a = 0; a < SI; ++a) {
+#pragma unroll
+      for (int b = 0; b < SJ; ++b) {
+        if (MODE == 0) {
+          acc[a][b] = mfma(p[a], q[b], acc[a][b]);
+        } else {
+          const f32x4 d = mfma(p[a], q[b], zero);
+          f32x4& t = acc[a > 0 ? a - 1 : SI - 1][b];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            t[r] = MODE == 1 ? __builtin_fmaf(dprev[b][r], cs[b], t[r]) : __builtin_fmaf(dprev[b][r], rs[r] * cs[b], t[r]);
+          dprev[b] = d;
+        }
+      }
+      if (MODE != 0) {
+#pragma unroll
+        for (int b = 0; b < SJ; ++b) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, MODE == 1 ? 4 : 8, 0);
+        }
+      }
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int a = 0; a < SI; ++a)
+#pragma unroll
+    for (int b = 0; b < SJ; ++b) s += acc[a][b][0] + acc[a][b][1] + acc[a][b][2] + acc[a][b][3] + dprev[b][a & 3];
+  out[(size_t)blockIdx.x * M_THREADS + threadIdx.x] = s;
+}
+
+// LDS-fed: a 256 x 256 workgroup tile of one K block (64 KB: 256 P rows then
+// 256 Q rows of 128 bytes, 16-byte chunks XOR-swizzled by row as in the GEMM),
+// filled once; every iteration each wavefront reads its 8 P and 4 Q fragments.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row & 7) ^ ((row >> 3) & 1))) << 4);
+}
+
+__global__ __launch_bounds__(M_THREADS) void k_mfma_lds(const int* __restrict__ seed, const float* __restrict__ scales,
+                                                       float* __restrict__ out, int iters) {
+  __shared__ __align__(16) uint8_t tile[512 * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = wave % 2, wj = wave / 2, g = lane >> 4, r16 = lane & 15;
+  for (int i = tid; i < 512 * 128 / 4; i += M_THREADS) reinterpret_cast<int*>(tile)[i] = seed[i & 63] ^ i;
+  __syncthreads();
+  auto load_frag = [&](const uint8_t* t, int row) -> i32x8 {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(t + swz(row, 2 * g));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(t + swz(row, 2 * g + 1));
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  const uint8_t* tp = tile;
+  const uint8_t* tq = tile + 256 * 128;
+  const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 acc[SI][SJ];
+#pragma unroll
+  for (int a = 0; a < SI; ++a)
+#pragma unroll
+    for (int b = 0; b < SJ; ++b) acc[a][b] = zero;
+  float cs[SJ];
+#pragma unroll
+  for (int b = 0; b < SJ; ++b) cs[b] = scales[(lane + b) & 7];
+  f32x4 dprev[SJ];
+#pragma unroll
+  for (int b = 0; b < SJ; ++b) dprev[b] = zero;
+  for (int it = 0; it < iters; ++it) {
+    constexpr int PF = 2;
+    i32x8 ring[PF + 1];
+    ring[0] = load_frag(tp, wi * 128 + r16);
+    i32x8 qf[SJ];
+#pragma unroll
+    for (int b = 0; b < SJ; ++b) qf[b] = load_frag(tq, wj * 64 + b * 16 + r16);
+#pragma unroll
+    for (int a = 1; a < PF; ++a) ring[a] = load_frag(tp, wi * 128 + a * 16 + r16);
+#pragma unroll
+    for (int a = 0; a < SI; ++a) {
+      if (a + PF < SI) ring[(a + PF) % (PF + 1)] = load_frag(tp, wi * 128 + (a + PF) * 16 + r16);
+      const i32x8 pf = ring[a % (PF + 1)];
+#pragma unroll
+      for (int b = 0; b < SJ; ++b) {
+        const f32x4 d = mfma(pf, qf[b], zero);
+        f32x4& t = acc[a > 0 ? a - 1 : SI - 1][b];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = __builtin_fmaf(dprev[b][r], cs[b], t[r]);
+        dprev[b] = d;
+      }
+#pragma unroll
+      for (int b = 0; b < SJ; ++b) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int a = 0; a < SI; ++a)
+#pragma unroll
+    for (int b = 0; b < SJ; ++b) s += acc[a][b][0] + acc[a][b][1] + acc[a][b][2] + acc[a][b][3] + dprev[b][a & 3];
+  out[(size_t)blockIdx.x * M_THREADS + tid] = s;
+}
+
+// ------------------------------------------------------------------- main --
+template <typename F>
+static float time_ms(F launch, int reps) {
+  hipEvent_t e0, e1;
+  (void)hipEventCreate(&e0);
+  (void)hipEventCreate(&e1);
+  launch();
+  (void)hipDeviceSynchronize();
+  (void)hipEventRecord(e0, 0);
+  for (int r = 0; r < reps; ++r) launch();
+  (void)hipEventRecord(e1, 0);
+  (void)hipEventSynchronize(e1);
+  float ms = 0.0f;
+  (void)hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return ms / reps;
+}
+
+int main() {
+  int cus = 0, clk_khz = 0;
+  CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0));
+  CHECK(hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeClockRate, 0));
+  printf("{\"device\": {\"compute_units\": %d, \"max_clock_mhz\": %d}}\n", cus, clk_khz / 1000);
+  fflush(stdout);
+
+  const size_t bytes = (size_t)2 << 30;        // 2 GiB per buffer
+  const size_t n16 = bytes / 16;
+  u32x4 *a = nullptr, *b = nullptr;
+  uint32_t* sink = nullptr;
+  CHECK(hipMalloc(&a, bytes));
+  CHECK(hipMalloc(&b, bytes));
+  const int max_grid = cus * 32;
+  CHECK(hipMalloc(&sink, (size_t)max_grid * S_THREADS * sizeof(uint32_t)));
+  CHECK(hipMemset(a, 1, bytes));
+  CHECK(hipMemset(b, 0, bytes));
+  const int reps = 10;
+  // Each stream is timed for 4, 8, 16 and 32 workgroups of 256 lanes per
+  // compute unit and 1, 2 and 4 vectors in flight per lane; the best is the
+  // ceiling (n16 = 2^27 is a multiple of every U * grid * 256 with 256
+  // compute units, so every trip is whole).
+  struct Best {
+    const char* name;
+    double bytes_moved;
+    float ms = 1e30f;
+    int wgs = 0, u = 0;
+  };
+  Best st[5] = {{"copy", 2.0 * bytes}, {"copy_nt", 2.0 * bytes}, {"read", 1.0 * bytes}, {"write", 1.0 * bytes},
+                {"read2_write1", 1.5 * bytes}};
+  auto sweep = [&](int k, auto launch_u1, auto launch_u2, auto launch_u4) {
+    for (int wpc : {4, 8, 16, 32}) {
+      const int grid = cus * wpc;
+      for (int u : {1, 2, 4}) {
+        if (n16 % ((size_t)u * grid * S_THREADS)) continue;
+        const float ms = time_ms([&] {
+          if (u == 1) launch_u1(grid);
+          else if (u == 2) launch_u2(grid);
+          else launch_u4(grid);
+        }, reps);
+        if (ms < st[k].ms) { st[k].ms = ms; st[k].wgs = wpc; st[k].u = u; }
+      }
+    }
+  };
+#define LAUNCH(KERNEL, ...) [&](int grid) { hipLaunchKernelGGL(KERNEL, dim3(grid), dim3(S_THREADS), 0, 0, __VA_ARGS__); }
+  sweep(0, LAUNCH((k_copy<false, 1>), a, b, n16), LAUNCH((k_copy<false, 2>), a, b, n16), LAUNCH((k_copy<false, 4>), a, b, n16));
+  sweep(1, LAUNCH((k_copy<true, 1>), a, b, n16), LAUNCH((k_copy<true, 2>), a, b, n16), LAUNCH((k_copy<true, 4>), a, b, n16));
+  sweep(2, LAUNCH((k_read<1>), a, sink, n16), LAUNCH((k_read<2>), a, sink, n16), LAUNCH((k_read<4>), a, sink, n16));
+  sweep(3, LAUNCH((k_write<1>), b, n16), LAUNCH((k_write<2>), b, n16), LAUNCH((k_write<4>), b, n16));
+  sweep(4, LAUNCH((k_read2_write1<1>), a, reinterpret_cast<u32x2*>(b), n16),
+        LAUNCH((k_read2_write1<2>), a, reinterpret_cast<u32x2*>(b), n16),
+        LAUNCH((k_read2_write1<4>), a, reinterpret_cast<u32x2*>(b), n16));
+#undef LAUNCH
+  CHECK(hipGetLastError());
+
+  // the K-major order over [28672, 4096] byte matrices (a decode weight), a
+  // different 117 MB matrix of the 2 GiB buffer on every call so that none is
+  // read from the last-level cache: 448 workgroups of 64 rows, 128-, 256- and
+  // 512-byte segments per step
+  const int KR = 28672, KC = 4096;
+  const size_t mat = (size_t)KR * KC;
+  const int nmat = (int)(bytes / mat);          // 18
+  int call = 0;
+  auto next_mat = [&]() { return reinterpret_cast<const uint8_t*>(a) + (size_t)(call++ % nmat) * mat; };
+  Best km[3] = {{"kmajor_128", (double)mat}, {"kmajor_256", (double)mat}, {"kmajor_512", (double)mat}};
+  km[0].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor<128>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
+  km[1].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor<256>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
+  km[2].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor<512>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
+  CHECK(hipGetLastError());
+  for (const Best& s : st) {
+    const double gbs = s.bytes_moved / (s.ms * 1e-3) / 1e9;
+    printf("{\"stream\": \"%s\", \"ms\": %.4f, \"gbs\": %.1f, \"frac_hbm_peak\": %.4f, \"wg_per_cu\": %d, \"vectors_per_lane\": %d}\n",
+           s.name, s.ms, gbs, gbs / 8000.0, s.wgs, s.u);
+  }
+  for (const Best& s : km) {
+    const double gbs = s.bytes_moved / (s.ms * 1e-3) / 1e9;
+    printf("{\"stream\": \"%s\", \"ms\": %.4f, \"gbs\": %.1f, \"frac_hbm_peak\": %.4f}\n", s.name, s.ms, gbs, gbs / 8000.0);
+  }
+  fflush(stdout);
+  CHECK(hipFree(a));
+  CHECK(hipFree(b));
+  CHECK(hipFree(sink));
+
+  int* seed = nullptr;
+  float *scales = nullptr, *out = nullptr;
+  const int mgrid = cus * 4;                   // 4 rounds of one 8-wavefront workgroup per compute unit
+  CHECK(hipMalloc(&seed, 64 * sizeof(int)));
+  CHECK(hipMalloc(&scales, 8 * sizeof(float)));
+  CHECK(hipMalloc(&out, (size_t)mgrid * M_THREADS * sizeof(float)));
+  int hseed[64];
+  for (int i = 0; i < 64; ++i) hseed[i] = (int)(0x3A3A3A3Au ^ (uint32_t)(i * 0x01030507u)) & 0x3F3F3F3F;   // finite E4M3 bytes
+  float hsc[8] = {1e-3f, 2e-3f, 3e-3f, 4e-3f, 5e-3f, 6e-3f, 7e-3f, 8e-3f};
+  CHECK(hipMemcpy(seed, hseed, sizeof(hseed), hipMemcpyHostToDevice));
+  CHECK(hipMemcpy(scales, hsc, sizeof(hsc), hipMemcpyHostToDevice));
+  const int iters = 1000;
+  const double flop = (double)mgrid * (M_THREADS / 64) * SI * SJ * (double)iters * 2.0 * 16 * 16 * 128;
+  struct Loop {
+    const char* name;
+    float ms;
+  } lp[4];
+  lp[0] = {"mfma", time_ms([&] { hipLaunchKernelGGL(k_mfma<0>, dim3(mgrid), dim3(M_THREADS), 0, 0, seed, scales, out, iters); }, 5)};
+  lp[1] = {"mfma_fma4", time_ms([&] { hipLaunchKernelGGL(k_mfma<1>, dim3(mgrid), dim3(M_THREADS), 0, 0, seed, scales, out, iters); }, 5)};
+  lp[2] = {"mfma_valu8", time_ms([&] { hipLaunchKernelGGL(k_mfma<2>, dim3(mgrid), dim3(M_THREADS), 0, 0, seed, scales, out, iters); }, 5)};
+  lp[3] = {"mfma_lds", time_ms([&] { hipLaunchKernelGGL(k_mfma_lds, dim3(mgrid), dim3(M_THREADS), 0, 0, seed, scales, out, iters); }, 5)};
+  CHECK(hipGetLastError());
+  CHECK(hipDeviceSynchronize());
+  for (const Loop& l : lp) {
+    const double tf = flop / (l.ms * 1e-3) / 1e12;
+    printf("{\"loop\": \"%s\", \"ms\": %.4f, \"tflops\": %.1f, \"frac_fp8_peak\": %.4f}\n", l.name, l.ms, tf, tf / 5000.0);
+  }
+  CHECK(hipFree(seed));
+  CHECK(hipFree(scales));
+  CHECK(hipFree(out));
+  return 0;
+}
