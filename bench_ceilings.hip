@@ -16,8 +16,13 @@
 //   read2_write1  16-byte loads, 8-byte stores: the 1x128 quantizer's 2 B in,
 //               1 B out per element
 //   kmajor_SEG  a [28672, 4096] byte matrix (a decode weight) read by 448
-//               workgroups of 64 rows, SEG bytes of each row per step (the
-//               GEMM's K-block order is SEG = 128)
+//               workgroups of 64 rows, SEG bytes of each row per step, four
+//               consecutive steps requested together
+//   kmajor_ringD  the same matrix in the GEMM's order: one 128-byte segment of
+//               each row per step, D steps in flight, the next step's loads
+//               issued as each step is consumed
+//   kmajor_dmaD  the GEMM's order through the LDS DMA (its copy instruction)
+//               into a ring of D 8 KB stages
 // MFMA loops (8 wavefronts per compute unit, 2 per SIMD, operands in
 // registers, each wavefront a 128 x 64 tile = 8 x 4 MFMAs per K block, as the
 // GEMM's large tile):
@@ -135,6 +140,84 @@ __global__ __launch_bounds__(S_THREADS) void k_read_kmajor(const uint8_t* __rest
       for (int u = 0; u < 4; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
     }
   }
+  sink[(size_t)blockIdx.x * S_THREADS + t] = x;
+}
+
+// The same matrix in the GEMM's own order: each step reads one 128-byte
+// segment of each of the workgroup's 64 rows (8 lanes per row, two loads per
+// lane), and the loads of step c + D go out only when step c is consumed, so
+// a row's consecutive segments are requested one step apart (D steps in
+// flight per lane, no burst of consecutive segments).
+template <int D>
+__global__ __launch_bounds__(S_THREADS) void k_read_kmajor_ring(const uint8_t* __restrict__ src,
+                                                                uint32_t* __restrict__ sink, int C) {
+  const int t = threadIdx.x;
+  const uint8_t* base = src + (size_t)blockIdx.x * 64 * C + (size_t)(t / 8) * C + (t % 8) * 16;
+  const int steps = C / 128;                              // C is a multiple of 128 * D
+  u32x4 v[D][2];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    v[d][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + d * 128));
+    v[d][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)32 * C + d * 128));
+  }
+  uint32_t x = 0;
+  for (int c0 = 0; c0 < steps; c0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      x ^= v[d][0][0] ^ v[d][0][3] ^ v[d][1][0] ^ v[d][1][3];
+      const int cn = c0 + d + D < steps ? c0 + d + D : steps - 1;
+      v[d][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)cn * 128));
+      v[d][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)32 * C + (size_t)cn * 128));
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) x ^= v[d][0][1] ^ v[d][1][1];
+  sink[(size_t)blockIdx.x * S_THREADS + t] = x;
+}
+
+// The GEMM's order again, through the LDS DMA (global_load_lds_dwordx4, the
+// GEMM's copy instruction) into a ring of D stages of 8 KB instead of
+// registers: each step's copies go out when step c is consumed, then the
+// wavefront waits (vmcnt) until step c + 1 has landed. No barrier: each
+// wavefront copies and reads only its own 16 rows' part of the ring.
+template <int D>
+__global__ __launch_bounds__(S_THREADS) void k_read_kmajor_dma(const uint8_t* __restrict__ src,
+                                                               uint32_t* __restrict__ sink, int C) {
+  __shared__ __align__(16) uint8_t ring[D][64 * 128];
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const uint32_t ring_lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(
+      (__attribute__((address_space(3))) void*)&ring[0][0]));
+  // wavefront w copies rows 16w .. 16w+15 (two 8-row slabs of 1 KB) of each step
+  const uint8_t* base = src + (size_t)blockIdx.x * 64 * C + (size_t)(16 * w) * C;
+  const uint32_t voff = (uint32_t)((lane >> 3) * C + (lane & 7) * 16);
+  const int steps = C / 128;
+  auto copy = [&](int c, int slot) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint64_t sb = (uint64_t)(uintptr_t)(base + (size_t)(8 * h) * C + (size_t)c * 128);
+      const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(ring_lds + slot * 8192 + (16 * w + 8 * h) * 128));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(lds), "v"(voff),
+                      "s"(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(sb >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sb))
+                   : "memory", "m0");
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) copy(d, d);
+  uint32_t x = 0;
+  for (int c0 = 0; c0 < steps; c0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      // step c0 + d has landed when at most (D - 1) steps' copies (2 each) are in flight
+      __builtin_amdgcn_s_waitcnt(((2 * (D - 1)) & 15) | (((2 * (D - 1)) >> 4) << 14) | (7 << 4) | (15 << 8));
+      x ^= *reinterpret_cast<const uint32_t*>(&ring[d][(16 * w + (lane & 15)) * 128 + (lane >> 4) * 16]);
+      const int cn = c0 + d + D < steps ? c0 + d + D : steps - 1;
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0) only: the read above is done before the slot refills
+      copy(cn, d);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8) | 0);      // vmcnt(0)
   sink[(size_t)blockIdx.x * S_THREADS + t] = x;
 }
 
@@ -363,10 +446,16 @@ int main() {
   const int nmat = (int)(bytes / mat);          // 18
   int call = 0;
   auto next_mat = [&]() { return reinterpret_cast<const uint8_t*>(a) + (size_t)(call++ % nmat) * mat; };
-  Best km[3] = {{"kmajor_128", (double)mat}, {"kmajor_256", (double)mat}, {"kmajor_512", (double)mat}};
+  Best km[7] = {{"kmajor_128", (double)mat}, {"kmajor_256", (double)mat}, {"kmajor_512", (double)mat},
+                {"kmajor_ring4", (double)mat}, {"kmajor_ring8", (double)mat}, {"kmajor_dma4", (double)mat},
+                {"kmajor_dma8", (double)mat}};
   km[0].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor<128>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
   km[1].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor<256>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
   km[2].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor<512>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
+  km[3].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor_ring<4>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
+  km[4].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor_ring<8>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
+  km[5].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor_dma<4>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
+  km[6].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor_dma<8>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
   CHECK(hipGetLastError());
   for (const Best& s : st) {
     const double gbs = s.bytes_moved / (s.ms * 1e-3) / 1e9;
