@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--weights-prequantized", action="store_true",
                     help="quantize the weights once per input set outside the timed step "
                          "(rollout: weights change once per optimizer update)")
+    ap.add_argument("--no-stream", action="store_true",
+                    help="run decode-sized forward-only linears on the row-major tile forward instead of the "
+                         "weight-streaming layout and its forward")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph (one graph per input set) and "
                          "replayed: graph_ms_per_step")
@@ -118,7 +121,13 @@ def measured_ceilings():
 # 2 B read + 1 B written per element (1x128, 128x1, 128x128 without the
 # transposed copy) or 2 B read + 2 B written (dual, 128x128 with it).
 STREAM_FOR = {"quant_act": "read2_write1", "quant_transpose": "read2_write1", "quant_dual": "copy_nt",
-              "quant_weight": "copy_nt", "quant_weight_nt": "read2_write1"}
+              "quant_weight": "copy_nt", "quant_weight_nt": "read2_write1",
+              "quant_weight_stream": "read2_write1"}
+
+# Forward-only linears with at most this many tokens (decode) run on the
+# weight-streaming layout: the weight quantizer writes it, the stream forward
+# reads it (the same bytes as the row-major codes, rearranged).
+STREAM_MAX_TOKENS = 64
 
 
 def act_bytes(rows, cols):
@@ -136,8 +145,9 @@ def weight_bytes(n, k, transposed):
 class Linear:
     """Device buffers and the launch list of one linear layer."""
 
-    def __init__(self, lin, passes, seed, fq, inputs, torch, dual=True):
+    def __init__(self, lin, passes, seed, fq, inputs, torch, dual=True, stream=True):
         self.name, self.M, self.N, self.K = lin["name"], lin["M"], lin["N"], lin["K"]
+        self.stream = stream and tuple(passes) == ("fwd",) and lin["M"] <= STREAM_MAX_TOKENS
         M, N, K = self.M, self.N, self.K
         dev = "cuda"
         t = inputs.linear_tensors_device(lin, seed=seed)
@@ -174,16 +184,24 @@ class Linear:
         fwd, dgrad, wgrad = ("fwd" in self.passes), ("dgrad" in self.passes), ("wgrad" in self.passes)
         x_dual, dy_dual = self.dual and fwd and wgrad, self.dual and dgrad and wgrad
         L = []
-        L.append(("quant_weight" if self.wq_t is not None else "quant_weight_nt", f"{self.name}.w[{N},{K}]", 0,
-                  weight_bytes(N, K, self.wq_t is not None),
-                  lambda: fq.quantize_weight_128x128(self.w, self.wq_t is not None, self.wq, self.ws, self.wq_t)))
+        if self.stream:
+            # wq holds the codes in the weight-streaming layout
+            L.append(("quant_weight_stream", f"{self.name}.w_stream[{N},{K}]", 0, weight_bytes(N, K, False),
+                      lambda: fq.quantize_weight_128x128_stream(self.w, self.wq, self.ws)))
+        else:
+            L.append(("quant_weight" if self.wq_t is not None else "quant_weight_nt", f"{self.name}.w[{N},{K}]", 0,
+                      weight_bytes(N, K, self.wq_t is not None),
+                      lambda: fq.quantize_weight_128x128(self.w, self.wq_t is not None, self.wq, self.ws, self.wq_t)))
         if x_dual:
             L.append(("quant_dual", f"{self.name}.x_dual[{M},{K}]", 0, dual_bytes(M, K),
                       lambda: fq.quantize_dual_1x128_128x1(self.x, self.xq, self.xs, self.xq_t, self.xs_t)))
         elif fwd:
             L.append(("quant_act", f"{self.name}.x[{M},{K}]", 0, act_bytes(M, K),
                       lambda: fq.quantize_act_1x128(self.x, self.xq, self.xs)))
-        if fwd:
+        if fwd and self.stream:
+            L.append(("gemm_fwd", f"{self.name}.fwd_stream[{M}x{N}x{K}]", 2 * M * N * K, M * K + N * K + 2 * M * N,
+                      lambda: fq.fp8_gemm_fwd_stream(self.xq, self.xs, self.wq, self.ws, out=self.y)))
+        elif fwd:
             L.append(("gemm_fwd", f"{self.name}.fwd[{M}x{N}x{K}]", 2 * M * N * K, M * K + N * K + 2 * M * N,
                       lambda: fq.fp8_gemm_fwd(self.xq, self.xs, self.wq, self.ws, out=self.y)))
         if dy_dual:
@@ -405,7 +423,8 @@ def main():
     grouped = not args.no_grouped and "wgrad" in wl["passes"] and len(wl["linears"]) > 1
 
     def build_step(seed):
-        layers = [Linear(lin, wl["passes"], seed + 17 * i, fq, inputs, torch, dual=not args.separate_quant)
+        layers = [Linear(lin, wl["passes"], seed + 17 * i, fq, inputs, torch, dual=not args.separate_quant,
+                         stream=not args.no_stream)
                   for i, lin in enumerate(wl["linears"])]
         for layer in layers:
             layer.defer_wgrad = grouped
@@ -587,6 +606,8 @@ def main():
         "quant_ms_per_step": round(quant_ms, 3),
         "quantizers": "separate" if args.separate_quant else "dual",
         "wgrad_launch": "grouped" if grouped else "per linear",
+        "fwd_path": "weight-streaming layout" if any(l[1].split("[")[0].endswith("fwd_stream") for l in launches)
+                    else "row-major tiles",
         "input_sets": nsets,
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "weights": "quantized once per input set, outside the step" if args.weights_prequantized

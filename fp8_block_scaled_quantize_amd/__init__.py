@@ -22,6 +22,9 @@ a multiple of 128, Kg = Kp/128; channel counts are any multiple of 8):
     fp8_gemm_fwd(xq, xs, wq, ws, n=None)      -> y  [M,N] bf16   (Y = X W^T; N defaults to Np)
     fp8_gemm_dgrad(dyq, dys, wq_t, ws, k=None) -> dx [M,K] bf16  (dX = dY W; K defaults to Kp)
     fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t)  -> dw [N,K] bf16   (dW = dY^T X)
+    quantize_weight_128x128_stream(w) -> (wq_s, ws): the weight codes in the streaming layout
+    weight_stream_layout(wq)          -> wq_s: row-major codes rearranged for streaming
+    fp8_gemm_fwd_stream(xq, xs, wq_s, ws, n=None) -> y [M,N] bf16 (M <= 64; equals fp8_gemm_fwd)
     fp8_gemm_{fwd,dgrad,wgrad}_grouped(problems, outs=None)
                                       -> list of outputs; each problem is the tuple of
                                          tensors the plain call takes (fwd / dgrad: plus,
@@ -86,6 +89,9 @@ def load_library():
         "fp8_gemm_dgrad": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
         "fp8_gemm_wgrad": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
         "fp8bsq_cast_f32_e4m3": ([vp, vp, i64, vp], i32),
+        "quantize_weight_128x128_stream": ([vp, i64, i64, vp, vp, vp], i32),
+        "fp8_weight_stream_layout": ([vp, i64, i64, vp, vp], i32),
+        "fp8_gemm_fwd_stream": ([vp, vp, vp, vp, vp, i64, i64, i64, vp], i32),
         "fp8_gemm_fwd_grouped": ([ctypes.POINTER(GemmProblem), i32, vp], i32),
         "fp8_gemm_dgrad_grouped": ([ctypes.POINTER(GemmProblem), i32, vp], i32),
         "fp8_gemm_wgrad_grouped": ([ctypes.POINTER(GemmProblem), i32, vp], i32),
@@ -350,6 +356,49 @@ def fp8_gemm_dgrad_grouped(problems, outs=None):
 def fp8_gemm_wgrad_grouped(problems, outs=None):
     """problems: [(dyq_t, dys_t, xq_t, xs_t), ...] -> [dw, ...] in one launch."""
     return _grouped("wgrad", problems, outs)
+
+
+def quantize_weight_128x128_stream(w, wq_s=None, ws=None):
+    """W [N, K] bf16 -> (wq_s [Np, Kp] u8 codes in the weight-streaming layout,
+    ws [Ng, Kg] f32), for fp8_gemm_fwd_stream."""
+    import torch
+    N, K = w.shape
+    _need(w, "w", torch.bfloat16, (N, K))
+    wq_s = _out(wq_s, "wq_s", torch.uint8, (padded(N), padded(K)), w)
+    ws = _out(ws, "ws", torch.float32, (padded(N) // 128, padded(K) // 128), w)
+    _check("quantize_weight_128x128_stream", load_library().quantize_weight_128x128_stream(
+        _ptr(w), N, K, _ptr(wq_s), _ptr(ws), _stream(w)))
+    return wq_s, ws
+
+
+def weight_stream_layout(wq, out=None):
+    """wq [Np, Kp] codes -> the same codes in the weight-streaming layout
+    (a uint8 tensor of the same shape; its bytes are arranged as
+    include/fp8bsq.h describes, not row-major)."""
+    import torch
+    Np, Kp = wq.shape
+    _need(wq, "wq", torch.uint8, (Np, Kp))
+    o = _out(out, "out", torch.uint8, (Np, Kp), wq)
+    _check("fp8_weight_stream_layout", load_library().fp8_weight_stream_layout(
+        _ptr(wq), Np, Kp, _ptr(o), _stream(wq)))
+    return o
+
+
+def fp8_gemm_fwd_stream(xq, xs, wq_s, ws, out=None, n=None):
+    """Y [M, N] = Xq Wq^T for M <= 64 tokens, the weight in its stream layout
+    (bit-identical to fp8_gemm_fwd on wq)."""
+    import torch
+    M, Kp = xq.shape
+    Np = wq_s.shape[0]
+    N = _cols(n, Np, "n")
+    _need(xq, "xq", torch.uint8, (M, Kp))
+    _need(xs, "xs", torch.float32, (M, Kp // 128))
+    _need(wq_s, "wq_s", torch.uint8, (Np, Kp))
+    _need(ws, "ws", torch.float32, (Np // 128, Kp // 128))
+    y = _out(out, "out", torch.bfloat16, (M, N), xq)
+    _check("fp8_gemm_fwd_stream", load_library().fp8_gemm_fwd_stream(
+        _ptr(xq), _ptr(xs), _ptr(wq_s), _ptr(ws), _ptr(y), M, N, Kp, _stream(xq)))
+    return y
 
 
 def cast_f32_e4m3(v, out=None):

@@ -14,6 +14,7 @@ namespace {
 constexpr int64_t kMaxDim = (int64_t)1 << 31;   // every dimension < 2^31
 constexpr int64_t kMaxElems = (int64_t)1 << 40;  // every tensor < 2^40 elements
 constexpr int64_t kMaxContraction = (int64_t)1 << 24;  // GEMM contraction length < 2^24
+constexpr int64_t kStreamMaxTokens = 64;                // token rows of fp8_gemm_fwd_stream at most
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
@@ -205,6 +206,33 @@ int fp8_gemm_dgrad_grouped(const fp8bsq_gemm_problem* problems, int count, void*
 
 int fp8_gemm_wgrad_grouped(const fp8bsq_gemm_problem* problems, int count, void* stream) {
   return gemm_grouped(Role::Wgrad, problems, count, stream);
+}
+
+int quantize_weight_128x128_stream(const void* w, int64_t N, int64_t K, uint8_t* wq_s, float* ws, void* stream) {
+  if (!dims_ok(N, K) || !dims_ok(round128(N), round128(K)) || !channels_ok(N) || !channels_ok(K))
+    return FP8BSQ_ERR_SHAPE;
+  if (N == 0 || K == 0) return FP8BSQ_OK;
+  if (!w || !wq_s || !ws) return FP8BSQ_ERR_NULL;
+  if (!aligned16(w) || !aligned16(wq_s) || !aligned16(ws)) return FP8BSQ_ERR_ALIGN;
+  return hip_status(fp8bsq::launch_quant_weight_stream(w, N, K, wq_s, ws, as_stream(stream)));
+}
+
+int fp8_weight_stream_layout(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wq_s, void* stream) {
+  if (!dims_ok(N, K) || !dims_ok(round128(N), round128(K)) || !channels_ok(N) || !channels_ok(K))
+    return FP8BSQ_ERR_SHAPE;
+  if (N == 0 || K == 0) return FP8BSQ_OK;
+  if (!wq || !wq_s) return FP8BSQ_ERR_NULL;
+  if (!aligned16(wq) || !aligned16(wq_s)) return FP8BSQ_ERR_ALIGN;
+  return hip_status(fp8bsq::launch_weight_stream_layout(wq, round128(N), round128(K), wq_s, as_stream(stream)));
+}
+
+int fp8_gemm_fwd_stream(const uint8_t* xq, const float* xs, const uint8_t* wq_s, const float* ws, void* y,
+                        int64_t M, int64_t N, int64_t K, void* stream) {
+  const fp8bsq_gemm_problem pr{xq, xs, wq_s, ws, y, M, N, K};
+  if (M > kStreamMaxTokens) return FP8BSQ_ERR_SHAPE;
+  const int st = check_problem(Role::Fwd, pr);
+  if (st != kLaunch) return st;
+  return hip_status(fp8bsq::launch_gemm_fwd_stream(xq, xs, wq_s, ws, y, M, N, K, as_stream(stream)));
 }
 
 int fp8bsq_cast_f32_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {

@@ -135,4 +135,37 @@ __device__ __forceinline__ float max64(float v) {
   return v;
 }
 
+// Asynchronous global -> LDS copies ("LDS DMA"): every lane of the wavefront
+// sends SIZE bytes from (sbase + voff) to LDS byte address lds + SIZE * lane.
+// sbase and lds are wavefront-uniform (SGPR pair / M0), voff is a per-lane
+// 32-bit offset. Written as inline assembly so the compiler neither keeps
+// 64-bit per-lane pointers live nor inserts waits for these copies before
+// unrelated LDS reads; the kernel waits for them itself (a vmcnt wait before
+// each barrier). The s_nop is the wait state a copy needs after M0 is written.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ uint64_t uniform_ptr(const void* ptr) {
+  const uint64_t v = (uint64_t)(uintptr_t)ptr;
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+}
+// LDS byte address of a __shared__ object (wavefront-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const void* lds) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void*)lds);
+}
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(uniform_ptr(sbase)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds), "v"(voff), "s"(uniform_ptr(sbase)) : "memory", "m0");
+}
+// Wait until at most N vector-memory operations of this wavefront are in
+// flight (they complete in order), leaving LDS and export counters alone.
+template <int N>
+__device__ __forceinline__ void wait_dma_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 }  // namespace fp8bsq

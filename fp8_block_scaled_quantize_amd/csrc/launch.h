@@ -47,4 +47,14 @@ hipError_t launch_gemm_wgrad(const uint8_t* dyq_t, const float* dys_t, const uin
                              const float* xs_t, void* dw, int64_t M, int64_t N, int64_t K,
                              hipStream_t stream);
 
+// The 128x128 weight quantizer writing its codes in the weight-streaming
+// layout (quantize.hip), that layout made from row-major codes, and the
+// forward for at most 64 token rows that reads it (stream.hip).
+hipError_t launch_quant_weight_stream(const void* w, int64_t N, int64_t K, uint8_t* wq_s, float* ws,
+                                      hipStream_t stream);
+hipError_t launch_weight_stream_layout(const uint8_t* wq, int64_t Np, int64_t Kp, uint8_t* wq_s,
+                                       hipStream_t stream);
+hipError_t launch_gemm_fwd_stream(const uint8_t* xq, const float* xs, const uint8_t* wq_s, const float* ws,
+                                  void* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 }  // namespace fp8bsq

@@ -132,12 +132,16 @@ __device__ __forceinline__ void transpose4x4(const uint32_t r[4], uint32_t c[4])
 
 // The codes are [Np, Kp] (and wq_t [Kp, Np]), N and K rounded up to 128; in
 // the TAIL instantiation the rows past N and the channels past K read as +0.
-template <bool TAIL>
+// The STREAM instantiation writes the same codes in the weight-streaming
+// layout instead of row-major (and no transposed copy): the block's eight
+// 16-row fragments, each 2 KB in the order the MFMA's lanes hold them, meet
+// in LDS and leave as eight contiguous 2 KB runs (16-byte stores).
+template <bool TAIL, bool STREAM = false>
 __global__ __launch_bounds__(W_THREADS) void quant_weight_128x128_kernel(
     const uint16_t* __restrict__ w, uint8_t* __restrict__ wq, float* __restrict__ ws,
     uint8_t* __restrict__ wq_t, int N, int K, int Np, int Kp, int nb0) {
   __shared__ float red[W_THREADS / 64];
-  __shared__ __align__(16) uint8_t tile_t[128 * W_ROW_BYTES];
+  __shared__ __align__(16) uint8_t tile_t[128 * W_ROW_BYTES];   // 17 KB: also holds the 16 KB stream tile
   const int t = threadIdx.x;
   const int kb = blockIdx.x, nb = nb0 + (int)blockIdx.y;
   const int r0 = 8 * (t >> 4), c0 = 8 * (t & 15);
@@ -186,10 +190,33 @@ __global__ __launch_bounds__(W_THREADS) void quant_weight_128x128_kernel(
     for (int e = 0; e < 8; ++e) q[e] = quotient(v[e], d.sc, d.r);
     code[i][0] = e4m3x4_q(q[0], q[1], q[2], q[3]);
     code[i][1] = e4m3x4_q(q[4], q[5], q[6], q[7]);
-    __builtin_nontemporal_store(u32x2{code[i][0], code[i][1]},
-                                reinterpret_cast<u32x2*>(wq + (row0 + i) * Kp + col0));
+    if (!STREAM)
+      __builtin_nontemporal_store(u32x2{code[i][0], code[i][1]},
+                                  reinterpret_cast<u32x2*>(wq + (row0 + i) * Kp + col0));
   }
   if (t == 0) ws[(int64_t)nb * (Kp / 128) + kb] = s;
+
+  if (STREAM) {
+    // Row rl = r0 + i, channels c0 .. c0 + 7 of the block: fragment rl / 16,
+    // lane 16 (c0 / 32) + rl % 16, half (c0 / 16) % 2, bytes c0 % 16 .. + 7.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rl = r0 + i;
+      const int off = ((rl / 16) * 2 + (c0 / 16) % 2) * 1024 + 16 * (16 * (c0 / 32) + rl % 16) + c0 % 16;
+      *reinterpret_cast<u32x2*>(tile_t + off) = u32x2{code[i][0], code[i][1]};
+    }
+    __syncthreads();
+    const int64_t kbt = Kp / 128;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int piece = t + W_THREADS * j;                 // 16-byte piece of the 16 KB tile
+      const int fl = piece / 128;
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(tile_t + 16 * piece),
+                                  reinterpret_cast<u32x4*>(wq + (((int64_t)nb * 8 + fl) * kbt + kb) * 2048 +
+                                                           16 * (piece % 128)));
+    }
+    return;
+  }
 
   if (wq_t != nullptr) {
     // Transpose the 8x8 byte tile: out[j] holds column c0+j, rows r0..r0+7.
@@ -611,6 +638,25 @@ hipError_t launch_quant_weight_128x128(const void* w, int64_t N, int64_t K, uint
     else
       hipLaunchKernelGGL(quant_weight_128x128_kernel<false>, grid, dim3(W_THREADS), 0, stream,
                          static_cast<const uint16_t*>(w), wq, ws, wq_t, (int)N, (int)K, (int)N, (int)K, (int)y0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_stream(const void* w, int64_t N, int64_t K, uint8_t* wq_s, float* ws,
+                                      hipStream_t stream) {
+  const int64_t nbt = groups128(N), kbt = groups128(K);
+  const bool tail = N % 128 != 0 || K % 128 != 0;
+  for (int64_t y0 = 0; y0 < nbt; y0 += kMaxGridY) {
+    const int64_t ny = nbt - y0 < kMaxGridY ? nbt - y0 : kMaxGridY;
+    const dim3 grid((unsigned)kbt, (unsigned)ny);
+    if (tail)
+      hipLaunchKernelGGL((quant_weight_128x128_kernel<true, true>), grid, dim3(W_THREADS), 0, stream,
+                         static_cast<const uint16_t*>(w), wq_s, ws, nullptr, (int)N, (int)K, (int)(nbt * 128),
+                         (int)(kbt * 128), (int)y0);
+    else
+      hipLaunchKernelGGL((quant_weight_128x128_kernel<false, true>), grid, dim3(W_THREADS), 0, stream,
+                         static_cast<const uint16_t*>(w), wq_s, ws, nullptr, (int)N, (int)K, (int)N, (int)K,
+                         (int)y0);
   }
   return hipGetLastError();
 }

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FP8BSQ_ABI_VERSION 6
+#define FP8BSQ_ABI_VERSION 7
 
 /* Status codes. */
 #define FP8BSQ_OK 0
@@ -267,6 +267,54 @@ typedef struct fp8bsq_gemm_problem {
 int fp8_gemm_fwd_grouped(const fp8bsq_gemm_problem* problems, int count, void* stream);
 int fp8_gemm_dgrad_grouped(const fp8bsq_gemm_problem* problems, int count, void* stream);
 int fp8_gemm_wgrad_grouped(const fp8bsq_gemm_problem* problems, int count, void* stream);
+
+/*
+ * quantize_weight_128x128_stream -- quantize_weight_128x128 with its codes
+ * written in the weight-streaming layout (see fp8_weight_stream_layout)
+ * instead of row-major, for weights that only feed fp8_gemm_fwd_stream.
+ * Source: as quantize_weight_128x128.
+ *
+ *   w    in : bf16 [N, K] row-major
+ *   wq_s out: E4M3, Np * Kp bytes, byte-identical to
+ *             fp8_weight_stream_layout(wq) of quantize_weight_128x128's wq
+ *   ws   out: fp32 [Ng, Kg], as quantize_weight_128x128
+ * Shape: N % 8 == 0, K % 8 == 0. No transposed copy.
+ */
+int quantize_weight_128x128_stream(const void* w, int64_t N, int64_t K, uint8_t* wq_s, float* ws, void* stream);
+
+/*
+ * fp8_weight_stream_layout -- the weight codes rearranged for streaming.
+ * Source: "Arquitectura Central" (rollout runs the training forward's FP8
+ * flow on the same 128x128-block weight codes, refreshed once per optimizer
+ * update) and "Esquema de Cuantización" (the 128x128 weight quantization).
+ * The same codes in another order, made once per weight version, for
+ * fp8_gemm_fwd_stream: no arithmetic, no rounding.
+ *
+ *   wq   in : E4M3 [Np, Kp]      (wq of quantize_weight_128x128)
+ *   wq_s out: E4M3, Np * Kp bytes: with Kb = Kp/128, for 16-row fragment f,
+ *             K block kb, half h (0/1), lane l = 16 g + r (g < 4, r < 16) and
+ *             byte b < 16:
+ *               wq_s[((f*Kb + kb)*2 + h)*1024 + 16*l + b] = wq[(16f + r)*Kp + 128kb + 32g + 16h + b]
+ *             i.e. each 16-row x 128-byte block of wq as 2 KB of contiguous
+ *             bytes, blocks of one 16-row band in K order.
+ * N, K are the weight's logical sizes. Shape: N % 8 == 0, K % 8 == 0.
+ */
+int fp8_weight_stream_layout(const uint8_t* wq, int64_t N, int64_t K, uint8_t* wq_s, void* stream);
+
+/*
+ * fp8_gemm_fwd_stream -- the forward / rollout GEMM of fp8_gemm_fwd for at most
+ * 64 token rows (decode), reading the weight in its stream layout.
+ * Source: the same passages as fp8_gemm_fwd.
+ *
+ *   xq in : E4M3 [M, Kp], xs in: fp32 [M, Kg]         (from quantize_act_1x128)
+ *   wq_s in: fp8_weight_stream_layout of wq [Np, Kp], ws in: fp32 [Ng, Kg]
+ *   y  out: bf16 [M, N], bit-identical to fp8_gemm_fwd(xq, xs, wq, ws, y, M, N, K)
+ * For decode the GEMM is bound by reading the weight once; the stream layout
+ * lets each wavefront read its weight rows as one sequential stream.
+ * Shape: 1 <= M <= 64 (M = 0 is a no-op), N % 8 == 0, K % 8 == 0, Kp < 2^24.
+ */
+int fp8_gemm_fwd_stream(const uint8_t* xq, const float* xs, const uint8_t* wq_s, const float* ws, void* y,
+                        int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * fp8bsq_cast_f32_e4m3 -- the library's E4M3 encoder on its own.

@@ -60,3 +60,37 @@ def assert_bytes_equal(got, want, what, x_bits=None):
             extra = f" input bits {x_bits[t]:04x}" if x_bits is not None and x_bits.shape == got.shape else ""
             lines.append(f"  {t}: gpu={got[t]!r} want={want[t]!r}{extra}")
         raise AssertionError("\n".join(lines))
+
+
+def one_per_tile(n, seed, group=1, band=256):
+    """Indices with one `group`-wide unit inside every `band`-wide band of [0, n), plus the last unit."""
+    rng = np.random.default_rng(seed)
+    units = []
+    for t in range((n + band - 1) // band):
+        lo, hi = band * t // group, min(band * t + band, n) // group
+        units.append(int(rng.integers(lo, hi)))
+    units = sorted(set(units) | {n // group - 1})
+    return np.concatenate([np.arange(u * group, u * group + group) for u in units])
+
+
+_weight_cache = {}
+
+
+def oracle_weight(w):
+    """oracle.quant.quantize_weight_128x128 of a device bf16 weight: (codes, scales).
+
+    The 128x128 blocks are independent, so 128-row bands are quantized in
+    threads and stacked. The last result is cached by the weight's bytes.
+    """
+    import hashlib
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import quant
+    bits = host_bits(w)
+    key = hashlib.sha256(bits.tobytes()).hexdigest()
+    if key not in _weight_cache:
+        bands = [bits[r:r + 128] for r in range(0, bits.shape[0], 128)]
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            parts = list(ex.map(quant.quantize_weight_128x128, bands))
+        _weight_cache.clear()
+        _weight_cache[key] = (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]))
+    return _weight_cache[key]

@@ -32,14 +32,15 @@ def test_every_declared_symbol_is_exported(lib):
                           "quantize_dual_1x128_128x1", "rmsnorm_quantize_1x128", "swiglu_quantize_1x128",
                           "fp8_gemm_fwd", "fp8_gemm_fwd_grouped", "fp8_gemm_dgrad_grouped",
                           "fp8_gemm_wgrad_grouped", "fp8_gemm_dgrad", "fp8_gemm_wgrad",
-                          "fp8bsq_strerror", "fp8bsq_abi_version", "fp8bsq_cast_f32_e4m3"}
+                          "fp8bsq_strerror", "fp8bsq_abi_version", "fp8bsq_cast_f32_e4m3",
+                          "fp8_weight_stream_layout", "fp8_gemm_fwd_stream", "quantize_weight_128x128_stream"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_strerror(lib):
     lib.fp8bsq_abi_version.restype = ctypes.c_int
-    assert lib.fp8bsq_abi_version() == 6
+    assert lib.fp8bsq_abi_version() == 7
     lib.fp8bsq_strerror.restype = ctypes.c_char_p
     lib.fp8bsq_strerror.argtypes = [ctypes.c_int]
     for code in range(5):
@@ -177,3 +178,30 @@ def test_binding_has_no_cpu_fallback():
             if fn.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle|import_module\(.oracle|oracle\.", text, re.M), fn
+
+
+def test_stream_layout_validation(lib):
+    q = lib.quantize_weight_128x128_stream
+    q.argtypes = [P, I64, I64, P, P, P]
+    q.restype = ctypes.c_int
+    assert q(FAKE, 100, 128, FAKE, FAKE, None) == 2           # N a multiple of 8
+    assert q(None, 136, 200, FAKE, FAKE, None) == 1           # partial blocks pass the shape check
+    assert q(FAKE, 128, 128, FAKE, None, None) == 1
+    assert q(FAKE, 128, 128, MISALIGNED, FAKE, None) == 3
+    assert q(None, 0, 128, None, None, None) == 0             # empty: no-op
+    s = lib.fp8_weight_stream_layout
+    s.argtypes = [P, I64, I64, P, P]
+    s.restype = ctypes.c_int
+    assert s(FAKE, 128, 100, FAKE, None) == 2
+    assert s(FAKE, 128, 128, None, None) == 1
+    assert s(MISALIGNED, 128, 128, FAKE, None) == 3
+    assert s(None, 128, 0, None, None) == 0
+    f = lib.fp8_gemm_fwd_stream
+    f.argtypes = [P, P, P, P, P, I64, I64, I64, P]
+    f.restype = ctypes.c_int
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 65, 128, 128, None) == 2    # at most 64 token rows
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 64, 128, 128, None) == 1    # 64 rows pass the shape check
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 100, 128, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, MISALIGNED, 1, 128, 128, None) == 3
+    assert f(None, None, None, None, None, 0, 128, 128, None) == 0     # M == 0: no-op
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 128, 0, None) == 2       # empty contraction

@@ -23,7 +23,7 @@ import torch
 import fp8_block_scaled_quantize_amd as fq
 from fp8_block_scaled_quantize_amd import inputs
 from oracle import gemm, quant
-from tests._gpu import dev_bf16, dev_f32, dev_u8, host_bits, note, requires_gpu
+from tests._gpu import dev_bf16, dev_f32, dev_u8, host_bits, note, one_per_tile, oracle_weight, requires_gpu
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -213,17 +213,6 @@ def test_exact_large_tiles_wgrad(grid):
 # extent in each dimension) is checked against the oracle, so a tile computed
 # in the wrong place or not at all would show.
 
-def _one_per_tile(n, seed, group=1, band=256):
-    """Indices with one `group`-wide unit inside every `band`-wide band of [0, n), plus the last unit."""
-    rng = np.random.default_rng(seed)
-    units = []
-    for t in range((n + band - 1) // band):
-        lo, hi = band * t // group, min(band * t + band, n) // group
-        units.append(int(rng.integers(lo, hi)))
-    units = sorted(set(units) | {n // group - 1})
-    return np.concatenate([np.arange(u * group, u * group + group) for u in units])
-
-
 @pytest.mark.parametrize("config,rows_j", [("large", 5504), ("medium", 3520)])
 @pytest.mark.parametrize("role", ["fwd", "dgrad", "wgrad"])
 def test_every_tile_long_contraction(role, config, rows_j):
@@ -244,7 +233,7 @@ def test_every_tile_long_contraction(role, config, rows_j):
         wq, ws, _ = fq.quantize_weight_128x128(w, transposed=False)
         out = fq.fp8_gemm_fwd(xq, xs, wq, ws)
         torch.cuda.synchronize()
-        r, c = _one_per_tile(M, 1, band=jband), _one_per_tile(N, 2, group=128)
+        r, c = one_per_tile(M, 1, band=jband), one_per_tile(N, 2, group=128)
         oxq, oxs = quant.quantize_act_1x128(host_bits(x[r]))
         owq, ows, _ = quant.quantize_weight_128x128(host_bits(w[c]))
         ref = gemm.gemm_fwd(oxq, oxs, owq, ows)
@@ -253,7 +242,7 @@ def test_every_tile_long_contraction(role, config, rows_j):
         wq, ws, wq_t = fq.quantize_weight_128x128(w)
         out = fq.fp8_gemm_dgrad(dyq, dys, wq_t, ws)
         torch.cuda.synchronize()
-        r, c = _one_per_tile(M, 3, band=jband), _one_per_tile(K, 4, group=128)
+        r, c = one_per_tile(M, 3, band=jband), one_per_tile(K, 4, group=128)
         odq, ods = quant.quantize_act_1x128(host_bits(dy[r]))
         owq, ows, _ = quant.quantize_weight_128x128(host_bits(w[:, c]))
         ref = gemm.gemm_dgrad(odq, ods, owq, ows)
@@ -262,7 +251,7 @@ def test_every_tile_long_contraction(role, config, rows_j):
         xq_t, xs_t = fq.transpose_quantize_128x1(x)
         out = fq.fp8_gemm_wgrad(dyq_t, dys_t, xq_t, xs_t)
         torch.cuda.synchronize()
-        r, c = _one_per_tile(N, 5, band=jband), _one_per_tile(K, 6)
+        r, c = one_per_tile(N, 5, band=jband), one_per_tile(K, 6)
         oq1, os1 = quant.transpose_quantize_128x1(host_bits(dy[:, r]))
         oq2, os2 = quant.transpose_quantize_128x1(host_bits(x[:, c]))
         ref = gemm.gemm_wgrad(oq1, os1, oq2, os2)
@@ -426,24 +415,6 @@ def test_gemm_determinism():
 
 TILE_BAND = 64
 
-_weight_cache = {}
-
-
-def _oracle_weight(w):
-    """oracle.quant.quantize_weight_128x128 of a device bf16 weight, by 128-row bands in threads."""
-    import hashlib
-    from concurrent.futures import ThreadPoolExecutor
-    bits = host_bits(w)
-    key = hashlib.sha256(bits.tobytes()).hexdigest()
-    if key not in _weight_cache:
-        bands = [bits[r:r + 128] for r in range(0, bits.shape[0], 128)]
-        with ThreadPoolExecutor(max_workers=16) as ex:
-            parts = list(ex.map(quant.quantize_weight_128x128, bands))
-        _weight_cache.clear()
-        _weight_cache[key] = (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]))
-    return _weight_cache[key]
-
-
 def _quantize_for_passes(x, dy, w, passes):
     """GPU quantization of one linear's operands, the way the benchmark step does it."""
     fwd, dgrad, wgrad = "fwd" in passes, "dgrad" in passes, "wgrad" in passes
@@ -475,13 +446,13 @@ def _check_linear(lin, passes, seed, keep_wgrad=False):
     q = _quantize_for_passes(x, dy, w, passes)
     kept = None
     if "fwd" in passes or "dgrad" in passes:
-        owq, ows = _oracle_weight(w)
+        owq, ows = oracle_weight(w)
     if "fwd" in passes:
         note(f"{lin['name']} fwd M={M} N={N} K={K}")
         y = fq.fp8_gemm_fwd(q["xq"], q["xs"], q["wq"], q["ws"])
         torch.cuda.synchronize()
-        rows = _one_per_tile(M, seed, band=TILE_BAND)
-        cols = _one_per_tile(N, seed + 1, band=TILE_BAND)
+        rows = one_per_tile(M, seed, band=TILE_BAND)
+        cols = one_per_tile(N, seed + 1, band=TILE_BAND)
         oxq, oxs = quant.quantize_act_1x128(host_bits(x[rows]))
         # rows `cols` of the dequantized weight: each weight row with its block's scales
         w_sel = gemm.dequant_rows(owq[cols], ows[cols // 128])
@@ -492,8 +463,8 @@ def _check_linear(lin, passes, seed, keep_wgrad=False):
         note(f"{lin['name']} dgrad M={M} N={N} K={K}")
         dx = fq.fp8_gemm_dgrad(q["dyq"], q["dys"], q["wq_t"], q["ws"])
         torch.cuda.synchronize()
-        rows = _one_per_tile(M, seed + 2, band=TILE_BAND)
-        cols = _one_per_tile(K, seed + 3, band=TILE_BAND)
+        rows = one_per_tile(M, seed + 2, band=TILE_BAND)
+        cols = one_per_tile(K, seed + 3, band=TILE_BAND)
         odq, ods = quant.quantize_act_1x128(host_bits(dy[rows]))
         # columns `cols` of the dequantized weight, as rows (contraction over N)
         w_sel = gemm.dequant_rows(np.ascontiguousarray(owq[:, cols].T), np.ascontiguousarray(ows[:, cols // 128].T))
@@ -504,8 +475,8 @@ def _check_linear(lin, passes, seed, keep_wgrad=False):
         note(f"{lin['name']} wgrad M={M} N={N} K={K}")
         dw = fq.fp8_gemm_wgrad(q["dyq_t"], q["dys_t"], q["xq_t"], q["xs_t"])
         torch.cuda.synchronize()
-        ns = _one_per_tile(N, seed + 4, band=TILE_BAND)
-        ks = _one_per_tile(K, seed + 5, band=TILE_BAND)
+        ns = one_per_tile(N, seed + 4, band=TILE_BAND)
+        ks = one_per_tile(K, seed + 5, band=TILE_BAND)
         oq1, os1 = quant.transpose_quantize_128x1(host_bits(dy[:, ns]))
         oq2, os2 = quant.transpose_quantize_128x1(host_bits(x[:, ks]))
         ref = gemm.gemm_wgrad(oq1, os1, oq2, os2)
