@@ -316,17 +316,20 @@ def measured_traffic(path, key):
 
     The summary holds FETCH_SIZE and WRITE_SIZE per launch, each scaled by the
     ratio of the known bytes of a plain copy kernel to what the same counter
-    read for it. It is ignored once the GEMM source has changed since the
-    counters were taken (the stored source hash no longer matches).
+    read for it. It is ignored once a kernel source it names has changed since
+    the counters were taken (a stored source hash no longer matches).
     """
     import hashlib
     if not os.path.exists(path):
         return None
     tr = json.load(open(path))
-    src = os.path.join(ROOT, "fp8_block_scaled_quantize_amd", "csrc", "gemm.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if tr.get("source_sha256_16", {}).get("gemm.hip") != h:
+    hashes = tr.get("source_sha256_16", {})
+    if not hashes:
         return None
+    for name, want in hashes.items():
+        src = os.path.join(ROOT, "fp8_block_scaled_quantize_amd", "csrc", name)
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != want:
+            return None
     return tr.get("bytes_per_launch", {}).get(key)
 
 

@@ -26,6 +26,8 @@ def _step(x, w, dy, out):
     fq.fp8_gemm_wgrad(out["dyq_t"], out["dys_t"], out["xq_t"], out["xs_t"], out=out["dw"])
     fq.quantize_act_1x128(x[:64], out["dq"], out["ds"])           # a decode-sized pair
     fq.fp8_gemm_fwd(out["dq"], out["ds"], out["wq"], out["ws"], out=out["dy64"])
+    fq.quantize_weight_128x128_stream(w, out["wq_s"], out["ws_s"])  # the decode path on the stream layout
+    fq.fp8_gemm_fwd_stream(out["dq"], out["ds"], out["wq_s"], out["ws_s"], out=out["ds64"])
 
 
 def _buffers(M, N, K):
@@ -35,7 +37,8 @@ def _buffers(M, N, K):
             "xq": e((M, K), u8), "xs": e((M, K // 128), f32), "xq_t": e((K, M), u8), "xs_t": e((K, M // 128), f32),
             "dyq": e((M, N), u8), "dys": e((M, N // 128), f32), "dyq_t": e((N, M), u8),
             "dys_t": e((N, M // 128), f32), "y": e((M, N), bf), "dx": e((M, K), bf), "dw": e((N, K), bf),
-            "dq": e((64, K), u8), "ds": e((64, K // 128), f32), "dy64": e((64, N), bf)}
+            "dq": e((64, K), u8), "ds": e((64, K // 128), f32), "dy64": e((64, N), bf),
+            "wq_s": e((N, K), u8), "ws_s": e((N // 128, K // 128), f32), "ds64": e((64, N), bf)}
 
 
 def test_graph_replays_equal_eager():
@@ -68,3 +71,4 @@ def test_graph_replays_equal_eager():
         assert torch.isfinite(junk)
         for name, ref in eager.items():
             assert torch.equal(graphed[name], ref), f"replay {rep}: {name} differs from the eager call"
+    assert torch.equal(eager["ds64"], eager["dy64"])   # the stream forward equals the tile forward
