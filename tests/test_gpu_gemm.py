@@ -65,7 +65,7 @@ def _check_exact_or_close(out_bits, ref, grid, what, amax_prod):
     possible product (amax_x * amax_w = 448^2 * sx * sw), plus the bf16
     rounding of the result (2^-8 |ref|).
 
-    The number of outputs outside the spec band 2^-7 |ref| + 1e-3
+    The number of outputs outside the tolerance band 2^-7 |ref| + 1e-3
     rms(ref) is printed: on these adversarial operands the MFMA's own error
     can exceed that band where the products cancel to a small result.
     """
@@ -74,7 +74,7 @@ def _check_exact_or_close(out_bits, ref, grid, what, amax_prod):
         return
     got = gemm.bf16_bits_to_f64(out_bits)
     _, ns = gemm.within_tolerance(out_bits, ref)
-    print(f"[gpu] wide-grid {what}: {ns['violations']} of {ref.size} outputs outside the north-star band "
+    print(f"[gpu] wide-grid {what}: {ns['violations']} of {ref.size} outputs outside the tolerance band "
           f"(worst err/bound {ns['worst_err_over_bound']:.3g})", flush=True)
     bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -10 * amax_prod
     bad = np.abs(got - ref) > bound
