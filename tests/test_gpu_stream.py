@@ -102,3 +102,38 @@ def test_decode_workload_full_size():
     ref = gemm.dequant_rows(oxq, oxs) @ gemm.dequant_rows(owq[cols], ows[cols // 128]).T
     ok, info = gemm.within_tolerance(host_bits(y[rows][:, cols]), ref)
     assert ok, f"decode stream fwd, {len(rows)} x {len(cols)} outputs: {info}"
+
+
+def _random_shapes(n, seed):
+    """n seeded (M, N, K): M in 1..64, N and K multiples of 8 up to 2048, ragged or not."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.integers(1, 65))
+        N = 8 * int(rng.integers(1, 257))
+        K = 8 * int(rng.integers(1, 257))
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes(24, 2027))
+def test_stream_random_shapes(M, N, K):
+    note(f"stream path on a random shape M={M} N={N} K={K}")
+    x = inputs.bf16_normal_device((M, K), 1.0, 0.01, seed=M * 7 + N + K)
+    w = inputs.bf16_normal_device((N, K), 0.02, 0.0, seed=M + N * 3 + K)
+    xq, xs = fq.quantize_act_1x128(x)
+    wq, ws, _ = fq.quantize_weight_128x128(w, transposed=False)
+    wq_s, ws_s = fq.quantize_weight_128x128_stream(w)
+    conv = fq.weight_stream_layout(wq)
+    y_tile = fq.fp8_gemm_fwd(xq, xs, wq, ws, n=N)
+    y_stream = fq.fp8_gemm_fwd_stream(xq, xs, wq_s, ws_s, n=N)
+    torch.cuda.synchronize()
+    assert torch.equal(wq_s, conv), "stream quantizer codes differ from the converted row-major codes"
+    assert torch.equal(ws_s, ws)
+    assert torch.equal(y_stream, y_tile), "stream and tile forwards differ"
+    if N * K <= 1 << 20:
+        owq, ows, _ = quant.quantize_weight_128x128(host_bits(w))
+        assert_bytes_equal(host(wq_s), stream_order(owq), "stream codes vs the oracle")
+        oxq, oxs = quant.quantize_act_1x128(host_bits(x))
+        ok, info = gemm.within_tolerance(host_bits(y_stream), gemm.gemm_fwd(oxq, oxs, owq, ows, n=N))
+        assert ok, info
