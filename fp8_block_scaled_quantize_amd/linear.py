@@ -14,35 +14,56 @@ Every step runs in the library's HIP kernels through the C ABI:
                                                   the transposed codes saved for WGrad
               quantize_act_1x128(X)               inference (gradients off or not needed)
               fp8_gemm_fwd                        Y = Xq Wq^T
+              fp8_gemm_fwd_stream                 inference with at most 64 tokens (decode),
+                                                  on the weight codes in their streaming
+                                                  layout (made once per weight version);
+                                                  the same bits as fp8_gemm_fwd
     backward  quantize_dual_1x128_128x1(dY)
               fp8_gemm_dgrad                      dX = dYq Wq
               fp8_gemm_wgrad                      dW = dYq^T Xq
-Both paths quantize X with the same 1x128 rule and call the same GEMM, so a
-row of Y does not depend on whether gradients are tracked, on the other rows
-of the batch, or on the batch size. Feature counts that are not a multiple of
+Both paths quantize X with the same 1x128 rule and run the same GEMM
+arithmetic (the streaming forward gives fp8_gemm_fwd's bits), so a row of Y
+does not depend on whether gradients are tracked, on the other rows of the
+batch, or on the batch size. Feature counts that are not a multiple of
 128 end in partial groups; the FP8 codes are then padded to whole groups with
 +0 codes and the GEMMs return the logical feature counts.
 """
 
 import torch
 
-from . import (fp8_gemm_dgrad, fp8_gemm_fwd, fp8_gemm_wgrad, quantize_act_1x128,
-               quantize_dual_1x128_128x1, quantize_weight_128x128)
+from . import (fp8_gemm_dgrad, fp8_gemm_fwd, fp8_gemm_fwd_stream, fp8_gemm_wgrad, quantize_act_1x128,
+               quantize_dual_1x128_128x1, quantize_weight_128x128, weight_stream_layout)
+
+# Token counts up to which inference runs the weight-streaming forward.
+STREAM_MAX_TOKENS = 64
 
 
 class _WeightCodes:
-    """FP8 codes of a bf16 weight, refreshed when the weight changes in place."""
+    """FP8 codes of a bf16 weight, refreshed when the weight changes in place.
+
+    The streaming-layout copy (the same codes rearranged, N x K more bytes) is
+    made from the row-major codes on the first decode-sized inference call of
+    a weight version.
+    """
 
     def __init__(self):
         self.key = None
         self.wq = self.ws = self.wq_t = None
+        self.wq_s = None
 
     def get(self, w):
         key = (w.data_ptr(), w._version, tuple(w.shape))
         if key != self.key:
             self.wq, self.ws, self.wq_t = quantize_weight_128x128(w.detach(), transposed=True)
+            self.wq_s = None
             self.key = key
         return self.wq, self.ws, self.wq_t
+
+    def get_stream(self, w):
+        self.get(w)
+        if self.wq_s is None:
+            self.wq_s = weight_stream_layout(self.wq)
+        return self.wq_s, self.ws
 
 
 class FP8LinearFunction(torch.autograd.Function):
@@ -74,9 +95,13 @@ class FP8LinearFunction(torch.autograd.Function):
 
 
 def fp8_linear_inference(x, w, codes):
-    """The rollout path: Y = Xq Wq^T with no state kept for a backward pass."""
-    wq, ws, _ = codes.get(w)
+    """The rollout path: Y = Xq Wq^T with no state kept for a backward pass
+    (the weight-streaming forward for at most STREAM_MAX_TOKENS tokens)."""
     xq, xs = quantize_act_1x128(x)
+    if x.shape[0] <= STREAM_MAX_TOKENS:
+        wq_s, ws = codes.get_stream(w)
+        return fp8_gemm_fwd_stream(xq, xs, wq_s, ws, n=w.shape[0])
+    wq, ws, _ = codes.get(w)
     return fp8_gemm_fwd(xq, xs, wq, ws, n=w.shape[0])
 
 

@@ -114,3 +114,27 @@ def test_training_with_a_ragged_token_count():
     o2, s2 = quant.transpose_quantize_128x1(xb)
     ok, info = gemm.within_tolerance(host_bits(lin.weight.grad), gemm.gemm_wgrad(o1, s1, o2, s2))
     assert ok, info
+
+
+@pytest.mark.parametrize("tokens", [1, 17, 64])
+def test_decode_inference_on_the_streaming_layout(tokens):
+    """Rollout with at most 64 tokens runs the weight-streaming forward; its rows
+    equal the training forward's, and after an in-place weight update it uses
+    the new codes (the streaming copy is remade)."""
+    K, N = 1024, 768
+    note(f"FP8Linear decode inference, {tokens} tokens, on the streaming layout")
+    lin = _layer(K, N, seed=63)
+    x = inputs.bf16_normal_device((tokens, K), 1.0, 0.01, seed=64)
+    y_train = lin(x.clone().requires_grad_(True))
+    w2 = inputs.bf16_normal_device((N, K), 0.02, 0.0, seed=65)
+    with torch.no_grad():
+        y_dec = lin(x)
+        assert lin._codes.wq_s is not None                  # the streaming path ran
+        lin.weight.copy_(w2)                                # new codes and scales
+        y_dec2 = lin(x)
+    xq, xs = fq.quantize_act_1x128(x)
+    wq, ws, _ = fq.quantize_weight_128x128(w2, transposed=False)
+    y_abi2 = fq.fp8_gemm_fwd(xq, xs, wq, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_dec, y_train.detach())
+    assert torch.equal(y_dec2, y_abi2)
