@@ -554,6 +554,11 @@ def main():
                                  "flop_per_byte": round(ai, 1),
                                  "bound": "mfma" if ai >= RIDGE else "hbm",
                                  "frac_attainable": round(tf / attainable_tflops(ai), 4)}
+            # the decode forward against a read of the same weight bytes in its own order
+            if ceilings and "fwd_stream" in p["key"] and "stream_ring8" in ceilings["streams"]:
+                gbs = p["bytes"] / (p["ms"] * 1e-3) / 1e9
+                kernels[p["key"]]["frac_stream_ceiling"] = round(gbs / ceilings["streams"]["stream_ring8"]["gbs"], 4)
+                kernels[p["key"]]["stream_ceiling"] = "stream_ring8"
         else:
             gbs = p["bytes"] / (p["ms"] * 1e-3) / 1e9
             kernels[p["key"]] = {"ms": round(p["ms"], 4), "gbs": round(gbs, 1),

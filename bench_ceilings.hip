@@ -23,6 +23,10 @@
 //               issued as each step is consumed
 //   kmajor_dmaD  the GEMM's order through the LDS DMA (its copy instruction)
 //               into a ring of D 8 KB stages
+//   stream_ring8  the same 117 MB in the weight-streaming layout's order, as
+//               the decode forward reads it: 256 workgroups of 7 reading
+//               wavefronts (and one idle one), each reading one 16-row
+//               fragment's 32 contiguous 2 KB K blocks in turn, 8 in flight
 // MFMA loops (8 wavefronts per compute unit, 2 per SIMD, operands in
 // registers, each wavefront a 128 x 64 tile = 8 x 4 MFMAs per K block, as the
 // GEMM's large tile):
@@ -173,6 +177,41 @@ __global__ __launch_bounds__(S_THREADS) void k_read_kmajor_ring(const uint8_t* _
 #pragma unroll
   for (int d = 0; d < D; ++d) x ^= v[d][0][1] ^ v[d][1][1];
   sink[(size_t)blockIdx.x * S_THREADS + t] = x;
+}
+
+// The weight-streaming layout's order: wavefront w of workgroup g reads
+// fragment 7 g + w, its kb_count K blocks of 2 KB one after another (two
+// 1 KB loads per block, a lane's 16 bytes at lane * 16 and 1 KB further), D
+// blocks in flight, the loads of block c + D issued as block c is consumed.
+// The eighth wavefront only writes its sink word (the decode forward's
+// staging wavefront is there).
+template <int D>
+__global__ __launch_bounds__(512) void k_read_stream(const uint8_t* __restrict__ src, uint32_t* __restrict__ sink,
+                                                     int kb_count, int nfrag) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  uint32_t x = 0;
+  if (wave < 7) {
+    const int f = min((int)blockIdx.x * 7 + wave, nfrag - 1);
+    const uint8_t* base = src + (size_t)f * kb_count * 2048 + lane * 16;
+    u32x4 v[D][2];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      v[d][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)d * 2048));
+      v[d][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)d * 2048 + 1024));
+    }
+    for (int c0 = 0; c0 < kb_count; c0 += D) {            // kb_count is a multiple of D
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        x ^= v[d][0][0] ^ v[d][0][3] ^ v[d][1][0] ^ v[d][1][3];
+        const int cn = c0 + d + D < kb_count ? c0 + d + D : kb_count - 1;
+        v[d][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)cn * 2048));
+        v[d][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)cn * 2048 + 1024));
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) x ^= v[d][0][1] ^ v[d][1][1];
+  }
+  sink[(size_t)blockIdx.x * 512 + t] = x;
 }
 
 // The GEMM's order again, through the LDS DMA (global_load_lds_dwordx4, the
@@ -446,9 +485,9 @@ int main() {
   const int nmat = (int)(bytes / mat);          // 18
   int call = 0;
   auto next_mat = [&]() { return reinterpret_cast<const uint8_t*>(a) + (size_t)(call++ % nmat) * mat; };
-  Best km[7] = {{"kmajor_128", (double)mat}, {"kmajor_256", (double)mat}, {"kmajor_512", (double)mat},
+  Best km[8] = {{"kmajor_128", (double)mat}, {"kmajor_256", (double)mat}, {"kmajor_512", (double)mat},
                 {"kmajor_ring4", (double)mat}, {"kmajor_ring8", (double)mat}, {"kmajor_dma4", (double)mat},
-                {"kmajor_dma8", (double)mat}};
+                {"kmajor_dma8", (double)mat}, {"stream_ring8", (double)mat}};
   km[0].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor<128>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
   km[1].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor<256>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
   km[2].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor<512>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
@@ -456,6 +495,8 @@ int main() {
   km[4].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor_ring<8>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
   km[5].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor_dma<4>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
   km[6].ms = time_ms([&] { hipLaunchKernelGGL(k_read_kmajor_dma<8>, dim3(KR / 64), dim3(S_THREADS), 0, 0, next_mat(), sink, KC); }, 17);
+  // 1792 fragments of 16 rows, 7 per workgroup: 256 workgroups (the sink holds 256 x 512 words)
+  km[7].ms = time_ms([&] { hipLaunchKernelGGL(k_read_stream<8>, dim3(KR / 16 / 7), dim3(512), 0, 0, next_mat(), sink, KC / 128, KR / 16); }, 17);
   CHECK(hipGetLastError());
   for (const Best& s : st) {
     const double gbs = s.bytes_moved / (s.ms * 1e-3) / 1e9;

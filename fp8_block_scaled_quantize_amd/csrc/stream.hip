@@ -89,8 +89,13 @@ hipError_t launch_weight_stream_layout(const uint8_t* wq, int64_t Np, int64_t Kp
 // finished reading before barrier c.
 // ---------------------------------------------------------------------------
 constexpr int ST_J = 64;     // token rows of one call at most
-constexpr int ST_D = 8;      // weight K blocks in flight per compute wavefront
-constexpr int ST_CH = 8;     // K blocks per staged chunk
+// Weight K blocks in flight per compute wavefront (D) and K blocks per staged
+// chunk (CH), by workgroup width: wide weights (5-7 fragments per workgroup)
+// take a 12-block ring with 4-block chunks, narrower ones an 8-block ring
+// with 8-block chunks (each measured the faster where it is used; D is a
+// multiple of CH).
+constexpr int ST_D_WIDE = 12, ST_CH_WIDE = 4;
+constexpr int ST_D_NARROW = 8, ST_CH_NARROW = 8;
 constexpr bool ST_NT = true; // weight loads marked non-temporal (read once)
 
 __device__ __forceinline__ int st_swz(int row, int chunk) {
@@ -106,10 +111,9 @@ struct StreamParams {
   int J, N, Np, Kp, Kb;
 };
 
-template <int W, int NB>
+template <int W, int NB, int CH, int ST_D>
 __global__ __launch_bounds__(64 * (W + 1)) void fp8_gemm_fwd_stream_kernel(StreamParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int CH = ST_CH;
   constexpr int RJ = 16 * NB;                           // token rows staged
   static_assert(NB >= 1 && RJ <= ST_J && ST_D % CH == 0, "stream tile");
   __shared__ __align__(16) uint8_t qt[2][CH][RJ * 128];
@@ -291,7 +295,9 @@ static int stream_waves(int nfrag) {
 template <int W, int NB>
 static hipError_t run_stream_nb(const StreamParams& p, hipStream_t stream) {
   const int nfrag = p.Np / 16;
-  hipLaunchKernelGGL((fp8_gemm_fwd_stream_kernel<W, NB>), dim3((unsigned)((nfrag + W - 1) / W)), dim3(64 * (W + 1)),
+  constexpr int CH = W >= 5 ? ST_CH_WIDE : ST_CH_NARROW;
+  constexpr int D = W >= 5 ? ST_D_WIDE : ST_D_NARROW;
+  hipLaunchKernelGGL((fp8_gemm_fwd_stream_kernel<W, NB, CH, D>), dim3((unsigned)((nfrag + W - 1) / W)), dim3(64 * (W + 1)),
                      0, stream, p);
   return hipGetLastError();
 }
