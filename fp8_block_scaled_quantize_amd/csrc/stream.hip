@@ -116,6 +116,7 @@ __global__ __launch_bounds__(64 * (W + 1)) void fp8_gemm_fwd_stream_kernel(Strea
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int RJ = 16 * NB;                           // token rows staged
   static_assert(NB >= 1 && RJ <= ST_J && ST_D % CH == 0, "stream tile");
+  static_assert((RJ * CH) % 64 == 0, "the staging wavefront copies a chunk's scales 64 at a time");
   __shared__ __align__(16) uint8_t qt[2][CH][RJ * 128];
   __shared__ __align__(16) float qsc[2][RJ * CH];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
