@@ -70,10 +70,13 @@ hipError_t launch_weight_stream_layout(const uint8_t* wq, int64_t Np, int64_t Kp
 // Forward for J <= 64 token rows on the stream layout. A workgroup has W
 // compute wavefronts, which own W consecutive 16-row weight fragments (W
 // chosen so that the grid is whole rounds of the 256 compute units: 7 for a
-// 28672-row weight), and one staging wavefront. The token rows (NB 16-row
+// 28672-row weight), and TS staging wavefronts. The token rows (NB 16-row
 // blocks, NB = ceil(J / 16)) pass through LDS a chunk of CH K blocks at a
-// time, double-buffered; their 16-byte pieces are XOR-swizzled by row so the
-// fragment reads are free of bank conflicts.
+// time, in a ring of L + 1 buffers with L chunks in flight; their 16-byte
+// pieces are XOR-swizzled by row so the fragment reads are free of bank
+// conflicts. Every compute unit reads the same token rows from L2 at about
+// the same time, so a chunk takes a long round trip; narrow weights (little
+// compute per chunk) need several chunks in flight to hide it.
 //
 // Each compute wavefront keeps the next ST_D K blocks of its fragment in
 // flight in registers (2 KB each). Loads complete in issue order for the
@@ -82,20 +85,15 @@ hipError_t launch_weight_stream_layout(const uint8_t* wq, int64_t Np, int64_t Kp
 // carries those loads instead, and the compute wavefronts' main loop has no
 // other loads and no branches, so their waits keep the ring outstanding.
 //
-// Chunk protocol (both sides pass the same nch barriers): before barrier 0
-// the stager writes chunk 0 to buffer 0. Between barriers c and c + 1 the
-// compute wavefronts read chunk c from buffer c & 1 while the stager writes
-// chunk c + 1 to the other buffer, whose chunk c - 1 every compute wavefront
-// finished reading before barrier c.
+// Chunk protocol (every wavefront passes the same nch barriers): chunk c
+// goes to buffer c mod (L + 1). Chunk 0 is in place at barrier 0; between
+// barriers c and c + 1 the compute wavefronts read chunk c while chunks up
+// to c + L are on their way, chunk c + L sent after barrier c into the
+// buffer whose chunk c - 1 every compute wavefront finished reading before
+// barrier c; the staging wavefront that sent chunk c + 1 waits for it
+// before barrier c + 1.
 // ---------------------------------------------------------------------------
 constexpr int ST_J = 64;     // token rows of one call at most
-// Weight K blocks in flight per compute wavefront (D) and K blocks per staged
-// chunk (CH), by workgroup width: wide weights (5-7 fragments per workgroup)
-// take a 12-block ring with 4-block chunks, narrower ones an 8-block ring
-// with 8-block chunks (each measured the faster where it is used; D is a
-// multiple of CH).
-constexpr int ST_D_WIDE = 12, ST_CH_WIDE = 4;
-constexpr int ST_D_NARROW = 8, ST_CH_NARROW = 8;
 constexpr bool ST_NT = true; // weight loads marked non-temporal (read once)
 
 __device__ __forceinline__ int st_swz(int row, int chunk) {
@@ -111,60 +109,69 @@ struct StreamParams {
   int J, N, Np, Kp, Kb;
 };
 
-template <int W, int NB, int CH, int ST_D>
-__global__ __launch_bounds__(64 * (W + 1)) void fp8_gemm_fwd_stream_kernel(StreamParams p) {
+template <int W, int NB, int CH, int ST_D, int TS, int LS>
+__global__ __launch_bounds__(64 * (W + TS)) void fp8_gemm_fwd_stream_kernel(StreamParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int RJ = 16 * NB;                           // token rows staged
-  static_assert(NB >= 1 && RJ <= ST_J && ST_D % CH == 0, "stream tile");
+  constexpr int L = TS * LS;                            // chunks ahead of the one being read
+  constexpr int NBUF = L + 1;
+  static_assert(NB >= 1 && RJ <= ST_J && ST_D % CH == 0 && LS >= 1, "stream tile");
   static_assert((RJ * CH) % 64 == 0, "the staging wavefront copies a chunk's scales 64 at a time");
-  __shared__ __align__(16) uint8_t qt[2][CH][RJ * 128];
-  __shared__ __align__(16) float qsc[2][RJ * CH];
+  __shared__ __align__(16) uint8_t qt[NBUF][CH][RJ * 128];
+  __shared__ __align__(16) float qsc[NBUF][RJ * CH];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Kb = p.Kb, J = p.J;
   const int nch = (Kb + CH - 1) / CH;
 
-  if (wave == W) {
-    // ---- staging wavefront: LDS DMA, no registers held. A chunk is
+  if (wave >= W) {
+    // ---- staging wavefront s of TS: LDS DMA, no registers held. A chunk is
     // CH * RJ / 8 copies of 1 KB (8 rows of one K block each, the row's
     // 16-byte pieces sent to their swizzled slots) and RJ * CH / 64 copies of
     // 4-byte scales (element e = row * CH + u). Rows past J repeat row J - 1
     // and K blocks past Kb repeat block Kb - 1 (never read for a result).
-    // Offsets are 32-bit: J Kp < 2^30 bytes.
-    // (The wait counter holds 63 copies: past 48 in flight each copy first
-    // waits for one to land.)
-    constexpr int TOPS = CH * RJ / 8;
-    auto guard = [&](int i) {
-      if (i >= 48) wait_dma_keep<47>();
-    };
-    auto dma_chunk = [&](int c, int buf) {
+    // Offsets are 32-bit: J Kp < 2^30 bytes. Chunk c is sent by staging
+    // wavefront c mod TS; each has at most LS chunks in flight (of any L
+    // consecutive chunks, LS are its own), which its wait counter holds.
+    constexpr int OPS = CH * RJ / 8 + RJ * CH / 64;
+    static_assert(LS * OPS < 64, "copies of a staging wavefront in flight");
+    static_assert(64 % CH == 0, "a lane's scale column is the same in every scale copy");
+    const int s = wave - W;
+    // lane parts of the offsets, the same for every chunk: token copy n
+    // covers rows (8 n) mod RJ + lane / 8 of K block 8 n / RJ; scale copy n
+    // covers element 64 n + lane, row (64 n + lane) / CH, column lane mod CH
+    uint32_t roff[RJ / 8], soff[RJ * CH / 64];
+#pragma unroll
+    for (int m = 0; m < RJ / 8; ++m) {
+      const int row = 8 * m + lane / 8;
+      const int piece = (lane % 8) ^ ((row & 7) ^ ((row >> 3) & 1));
+      roff[m] = (uint32_t)min(row, J - 1) * (uint32_t)p.Kp + (uint32_t)piece * 16u;
+    }
+#pragma unroll
+    for (int n = 0; n < RJ * CH / 64; ++n) soff[n] = (uint32_t)min((64 * n + lane) / CH, J - 1) * (uint32_t)Kb;
+    auto dma_chunk = [&](int c) {
+      const int buf = c % NBUF;
       const uint32_t tbase = lds_addr(&qt[buf][0][0]);
 #pragma unroll
-      for (int n = 0; n < TOPS; ++n) {
-        const int kl = n * 8 / RJ, row = (n * 8) % RJ + lane / 8;
-        const int piece = (lane % 8) ^ ((row & 7) ^ ((row >> 3) & 1));
-        const uint32_t off = (uint32_t)min(row, J - 1) * (uint32_t)p.Kp +
-                             (uint32_t)min(c * CH + kl, Kb - 1) * 128u + (uint32_t)piece * 16u;
-        guard(n);
-        dma16(p.xq, off, tbase + 1024u * n);
+      for (int n = 0; n < CH * RJ / 8; ++n) {
+        const uint32_t kcol = (uint32_t)min(c * CH + n * 8 / RJ, Kb - 1) * 128u;   // wavefront-uniform
+        dma16(p.xq, roff[n % (RJ / 8)] + kcol, tbase + 1024u * n);
       }
       const uint32_t sbase = lds_addr(&qsc[buf][0]);
+      const uint32_t scol = (uint32_t)min(c * CH + lane % CH, Kb - 1);
 #pragma unroll
-      for (int n = 0; n < RJ * CH / 64; ++n) {
-        const int e = 64 * n + lane;
-        const uint32_t off = (uint32_t)min(e / CH, J - 1) * (uint32_t)Kb + (uint32_t)min(c * CH + e % CH, Kb - 1);
-        guard(TOPS + n);
-        dma4(p.xs, 4u * off, sbase + 256u * n);
-      }
+      for (int n = 0; n < RJ * CH / 64; ++n) dma4(p.xs, 4u * (soff[n] + scol), sbase + 256u * n);
     };
-    dma_chunk(0, 0);
-    wait_dma_keep<0>();
-    dma_chunk(1, 1);                                    // buffer 1 is not read before barrier 1
-    __syncthreads();                                    // barrier 0: chunk 0 in place
+    for (int c = s; c < L; c += TS) dma_chunk(c);
+    if (s == 0) {
+      wait_dma_keep<(LS - 1) * OPS>();                  // chunk 0 in place
+      dma_chunk(L);                                     // buffer L holds no chunk yet
+    }
+    __syncthreads();                                    // barrier 0
     for (int c = 0; c + 1 < nch; ++c) {
-      wait_dma_keep<0>();
+      if (c > 0 && c % TS == s) dma_chunk(c + L);      // its buffer held chunk c - 1
+      if ((c + 1) % TS == s) wait_dma_keep<(LS - 1) * OPS>();   // chunk c + 1 in place
       __syncthreads();                                  // barrier c + 1: chunk c + 1 in place, chunk c read
-      if (c + 2 < nch) dma_chunk(c + 2, c & 1);
     }
     wait_dma_keep<0>();                                 // no copy into LDS outlives the workgroup
     return;
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(64 * (W + 1)) void fp8_gemm_fwd_stream_kernel(Strea
     for (int u = 0; u < ST_D; ++u) {
       const int kb = kb0 + u;
       const int c = kb / CH;
-      step(ring[u], sring[u], c & 1, u % CH);
+      step(ring[u], sring[u], c % NBUF, u % CH);
       ring[u] = pload(kb + ST_D);
       sring[u] = wsb[min(kb + ST_D, Kb - 1)];
       if (u % CH == CH - 1 && c + 1 < nch) __syncthreads();   // barrier c + 1
@@ -257,7 +264,7 @@ __global__ __launch_bounds__(64 * (W + 1)) void fp8_gemm_fwd_stream_kernel(Strea
     const int kb = kb0 + u;
     if (kb < Kb) {
       const int c = kb / CH;
-      step(ring[u], sring[u], c & 1, u % CH);
+      step(ring[u], sring[u], c % NBUF, u % CH);
       if (u % CH == CH - 1 && c + 1 < nch) __syncthreads();   // barrier c + 1
     }
   }
@@ -293,13 +300,27 @@ static int stream_waves(int nfrag) {
   return best;
 }
 
+// Staging of one call, by workgroup width W and token blocks NB: K blocks
+// per chunk (ch), weight ring depth per compute wavefront (d), staging
+// wavefronts (ts) and chunks in flight per staging wavefront (ls). Wide
+// weights keep one chunk in flight; narrow ones, whose compute wavefronts
+// have less work per chunk, keep several (their LDS ring 58-135 KB), and
+// with one token block a deeper weight ring (each measured the faster where
+// it is used).
+struct StreamCfg {
+  int ch, d, ts, ls;
+};
+constexpr StreamCfg stream_cfg(int w, int nb) {
+  if (w >= 5) return {4, 12, 1, 1};
+  return nb == 1 ? StreamCfg{4, 12, 1, 6} : nb == 2 ? StreamCfg{4, 8, 2, 3} : nb == 3 ? StreamCfg{4, 8, 2, 2} : StreamCfg{4, 8, 3, 1};
+}
+
 template <int W, int NB>
 static hipError_t run_stream_nb(const StreamParams& p, hipStream_t stream) {
   const int nfrag = p.Np / 16;
-  constexpr int CH = W >= 5 ? ST_CH_WIDE : ST_CH_NARROW;
-  constexpr int D = W >= 5 ? ST_D_WIDE : ST_D_NARROW;
-  hipLaunchKernelGGL((fp8_gemm_fwd_stream_kernel<W, NB, CH, D>), dim3((unsigned)((nfrag + W - 1) / W)), dim3(64 * (W + 1)),
-                     0, stream, p);
+  constexpr StreamCfg k = stream_cfg(W, NB);
+  hipLaunchKernelGGL((fp8_gemm_fwd_stream_kernel<W, NB, k.ch, k.d, k.ts, k.ls>), dim3((unsigned)((nfrag + W - 1) / W)),
+                     dim3(64 * (W + k.ts)), 0, stream, p);
   return hipGetLastError();
 }
 

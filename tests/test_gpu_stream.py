@@ -44,13 +44,17 @@ def test_stream_layout_of_oracle_codes(N, K):
 
 
 # (N, K): the workgroup width the launch picks for N (weight fragments per
-# workgroup, 1..7) and the K blocks (Kb < 8: the ring's tail only; 8: its main
-# loop only; otherwise both).
+# workgroup, 1..7) and the K blocks Kb, against the weight ring (12 blocks
+# for wide weights and for one token block, else 8: Kb below it runs the
+# ring's tail only, a multiple of it the main loop only) and the token ring
+# (4-block chunks, up to 6 in flight: Kb below 24 ends inside the first
+# chunks in flight).
 SHAPES = [
     (8, 8),            # width 1, Kb 1, everything ragged
     (128, 128),        # width 1, Kb 1
     (1000, 1000),      # width 1, Kb 8, ragged
     (384, 1152),       # width 1, Kb 9
+    (2048, 1536),      # width 1, Kb 12
     (5120, 5120),      # width 2, Kb 40
     (12288, 1024),     # width 3, Kb 8
     (14336, 4096),     # width 4, Kb 32
