@@ -19,7 +19,9 @@ quantizer and GEMM launch inside the timed region of K steps). The per-launch
 table comes from HIP events around every launch in a pass of the same K steps
 run just before the timed region; inside the timed region only the launch that
 takes the most time is bracketed by HIP events (on the stream the kernels run
-on), and `roofline` reports that launch with its average duration there.
+on), and `roofline` reports that launch with its average duration there (and
+the median and minimum over the K steps; every launch in `kernels` carries the
+same three from the instrumented pass).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload.
 
@@ -55,7 +57,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-producers", action="store_true",
@@ -136,6 +138,26 @@ def act_bytes(rows, cols):
 
 def dual_bytes(rows, cols):
     return rows * cols * 4 + rows * (cols // 128) * 4 + cols * (rows // 128) * 4
+
+
+def launch_stats(samples):
+    """Mean, median and minimum of one launch's per-step durations (ms)."""
+    v = sorted(samples)
+    n = len(v)
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return {"ms": sum(v) / n, "ms_median": med, "ms_min": v[0]}
+
+
+def host_cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def weight_bytes(n, k, transposed):
@@ -308,7 +330,8 @@ def cpu_baseline(inputs, wl, tokens=16384):
                       f"fwd/dgrad/wgrad in fp64, {dt:.1f} s wall; inputs drawn on the host (numpy PCG64, "
                       f"seed 0, the same recipe as the step's), not the step's device-drawn tensors",
             "inputs_sha256": {k: hashlib.sha256(t[k].tobytes()).hexdigest()[:16] for k in ("x", "w", "dy")},
-            "seconds": dt}
+            "seconds": dt, "blas_threads": int(threads), "host_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": host_cpu_model()}
 
 
 def measured_traffic(path, key):
@@ -485,8 +508,9 @@ def main():
             fn()
             ev[s][i][1].record(stream)
     torch.cuda.synchronize()
-    per_ms = [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
-              for i in range(len(launches))]
+    per_stats = [launch_stats([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)])
+                 for i in range(len(launches))]
+    per_ms = [st["ms"] for st in per_stats]
     dom_i = max(range(len(launches)), key=lambda i: per_ms[i])
 
     # The timed region: exactly K steps; HIP events bracket only the dominant
@@ -504,7 +528,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    dom_ms = sum(a.elapsed_time(b) for a, b in dev) / args.steps
+    dom_stats = launch_stats([a.elapsed_time(b) for a, b in dev])
+    dom_ms = dom_stats["ms"]
 
     graph_ms = None
     if args.graph:
@@ -537,7 +562,7 @@ def main():
     # Per-launch average durations (ms) from the instrumented pass.
     per = []
     for i, (kind, key, flops, nbytes, _) in enumerate(launches):
-        per.append({"kind": kind, "key": key, "ms": per_ms[i], "flops": flops, "bytes": nbytes})
+        per.append({"kind": kind, "key": key, "flops": flops, "bytes": nbytes, **per_stats[i]})
     gemm_flops = sum(p["flops"] for p in per)
     gemm_ms = sum(p["ms"] for p in per if p["flops"])
     quant_ms = sum(p["ms"] for p in per if not p["flops"])
@@ -548,7 +573,8 @@ def main():
         if p["flops"]:
             tf = p["flops"] / (p["ms"] * 1e-3) / 1e12
             ai = p["flops"] / p["bytes"]
-            kernels[p["key"]] = {"ms": round(p["ms"], 4), "tflops": round(tf, 1),
+            kernels[p["key"]] = {"ms": round(p["ms"], 4), "ms_median": round(p["ms_median"], 4),
+                                 "ms_min": round(p["ms_min"], 4), "tflops": round(tf, 1),
                                  "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
                                  "gbs": round(p["bytes"] / (p["ms"] * 1e-3) / 1e9, 1),
                                  "flop_per_byte": round(ai, 1),
@@ -561,7 +587,8 @@ def main():
                 kernels[p["key"]]["stream_ceiling"] = "stream_ring8"
         else:
             gbs = p["bytes"] / (p["ms"] * 1e-3) / 1e9
-            kernels[p["key"]] = {"ms": round(p["ms"], 4), "gbs": round(gbs, 1),
+            kernels[p["key"]] = {"ms": round(p["ms"], 4), "ms_median": round(p["ms_median"], 4),
+                                 "ms_min": round(p["ms_min"], 4), "gbs": round(gbs, 1),
                                  "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
             kind = p["kind"]
             if ceilings and STREAM_FOR.get(kind) in ceilings["streams"]:
@@ -588,6 +615,8 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof["kernel"] = dom["key"]
     roof["avg_ms"] = round(dom["ms"], 4)
+    roof["median_ms"] = round(dom_stats["ms_median"], 4)
+    roof["min_ms"] = round(dom_stats["ms_min"], 4)
     roof["traffic"] = measured_traffic(args.traffic_from or os.path.join(
         ROOT, "profiles", f"traffic_{args.workload}.json"), dom["key"])
 

@@ -81,3 +81,15 @@ def test_summarize_counters_sums_per_dispatch(tmp_path, capsys):
                                   "quant_weight_nt", "quant_weight_stream"])
 def test_every_quantizer_launch_has_a_stream_ceiling(kind):
     assert bench.STREAM_FOR[kind] in ("copy_nt", "read2_write1")
+
+
+def test_launch_stats_mean_median_min():
+    assert bench.launch_stats([3.0, 1.0, 2.0]) == {"ms": 2.0, "ms_median": 2.0, "ms_min": 1.0}
+    assert bench.launch_stats([4.0, 1.0, 2.0, 3.0]) == {"ms": 2.5, "ms_median": 2.5, "ms_min": 1.0}
+    assert bench.launch_stats([0.5]) == {"ms": 0.5, "ms_median": 0.5, "ms_min": 0.5}
+
+
+def test_default_warmup_is_at_least_five(monkeypatch):
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    args = bench.parse()
+    assert args.warmup >= 5 and args.steps >= 20 and args.gpus == 1
