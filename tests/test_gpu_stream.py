@@ -9,8 +9,10 @@
   1..64 tried, on shapes that run each workgroup width (1..7 weight
   fragments), K lengths that run the ring's main loop, its tail or both, and
   ragged N / K;
-* the decode workload at full size, quantized and multiplied as the
-  benchmark runs it, on one output in every 64 x 64 band against the oracle.
+* decode-sized linears at full size (the benchmark's gate/up workload and
+  narrower weights that run the multi-chunk token ring), quantized and
+  multiplied as the benchmark runs them, on one output in every 16 x 64 band
+  against the oracle.
 Calls go through the C ABI (via the Python binding).
 """
 
@@ -84,13 +86,26 @@ def test_stream_fwd_equals_tile_fwd(N, K):
     assert torch.equal(ws_s, ws)
 
 
-def test_decode_workload_full_size():
-    """The rollout decode linear as the benchmark runs it: 1x128 activations, the
-    weight quantized straight into the stream layout, the stream forward."""
-    wl = inputs.WORKLOADS["llama31_8b_decode_gate_up_m64"]
-    lin = wl["linears"][0]
-    M, N, K = lin["M"], lin["N"], lin["K"]
-    note(f"decode stream fwd M={M} N={N} K={K}")
+# Decode-sized linears at full size: the benchmark's gate/up workload (7
+# fragments per workgroup, one token chunk in flight), the 8B down projection
+# (one fragment per workgroup, 3 staging wavefronts, 28 chunks), the 32B o
+# projection (2 fragments per workgroup, 10 chunks) and the 8B qkv
+# projection at 40 tokens (3 token blocks, 2 staging wavefronts).
+DECODE_LINEARS = [
+    ("gate_up", 64, 28672, 4096),
+    ("down_8b", 64, 4096, 14336),
+    ("o_32b", 64, 5120, 5120),
+    ("qkv_8b", 40, 6144, 4096),
+]
+
+
+@pytest.mark.parametrize("name,M,N,K", DECODE_LINEARS)
+def test_decode_linear_full_size(name, M, N, K):
+    """A rollout decode linear as the benchmark runs it: 1x128 activations, the
+    weight quantized straight into the stream layout, the stream forward; one
+    output in every 16-token x 64-channel band against the oracle."""
+    lin = dict(inputs.WORKLOADS["llama31_8b_decode_gate_up_m64"]["linears"][0], name=name, M=M, N=N, K=K)
+    note(f"decode stream fwd {name} M={M} N={N} K={K}")
     t = inputs.linear_tensors_device(lin, seed=1000)
     x, w = t["x"], t["w"]
     xq, xs = fq.quantize_act_1x128(x)
@@ -105,7 +120,7 @@ def test_decode_workload_full_size():
     oxq, oxs = quant.quantize_act_1x128(host_bits(x[rows]))
     ref = gemm.dequant_rows(oxq, oxs) @ gemm.dequant_rows(owq[cols], ows[cols // 128]).T
     ok, info = gemm.within_tolerance(host_bits(y[rows][:, cols]), ref)
-    assert ok, f"decode stream fwd, {len(rows)} x {len(cols)} outputs: {info}"
+    assert ok, f"decode stream fwd {name}, {len(rows)} x {len(cols)} outputs: {info}"
 
 
 def _random_shapes(n, seed):
