@@ -81,8 +81,8 @@ hipError_t launch_weight_stream_layout(const uint8_t* wq, int64_t Np, int64_t Kp
 // Each compute wavefront keeps the next ST_D K blocks of its fragment in
 // flight in registers (2 KB each). Loads complete in issue order for the
 // wait counter, so a wavefront that also loaded token chunks would have to
-// drain its weight loads whenever a chunk had to land; the staging wavefront
-// carries those loads instead, and the compute wavefronts' main loop has no
+// drain its weight loads whenever a chunk had to land; the staging wavefronts
+// carry those loads instead, and the compute wavefronts' main loop has no
 // other loads and no branches, so their waits keep the ring outstanding.
 //
 // Chunk protocol (every wavefront passes the same nch barriers): chunk c
@@ -90,8 +90,9 @@ hipError_t launch_weight_stream_layout(const uint8_t* wq, int64_t Np, int64_t Kp
 // barriers c and c + 1 the compute wavefronts read chunk c while chunks up
 // to c + L are on their way, chunk c + L sent after barrier c into the
 // buffer whose chunk c - 1 every compute wavefront finished reading before
-// barrier c; the staging wavefront that sent chunk c + 1 waits for it
-// before barrier c + 1.
+// barrier c (chunk L, whose buffer has held nothing, goes out before barrier
+// 0); the staging wavefront that sent chunk c + 1 waits for it before
+// barrier c + 1.
 // ---------------------------------------------------------------------------
 constexpr int ST_J = 64;     // token rows of one call at most
 constexpr bool ST_NT = true; // weight loads marked non-temporal (read once)
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(64 * (W + TS)) void fp8_gemm_fwd_stream_kernel(Stre
   const int nch = (Kb + CH - 1) / CH;
 
   if (wave >= W) {
-    // ---- staging wavefront s of TS: LDS DMA, no registers held. A chunk is
+    // ---- staging wavefront s of TS: LDS DMA, no data held in registers. A chunk is
     // CH * RJ / 8 copies of 1 KB (8 rows of one K block each, the row's
     // 16-byte pieces sent to their swizzled slots) and RJ * CH / 64 copies of
     // 4-byte scales (element e = row * CH + u). Rows past J repeat row J - 1
