@@ -15,6 +15,10 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;   // every dimension < 2^31
 constexpr int64_t kMaxElems = (int64_t)1 << 40;  // every tensor < 2^40 elements
 constexpr int64_t kMaxContraction = (int64_t)1 << 24;  // GEMM contraction length < 2^24
 constexpr int64_t kStreamMaxTokens = 64;                // token rows of fp8_gemm_fwd_stream at most
+// Weight rows of fp8_gemm_fwd_stream below this: its launch runs at most 256
+// threads per 16-row fragment (one fragment per workgroup with three staging
+// wavefronts), so the grid stays under 2^32 threads.
+constexpr int64_t kStreamMaxRows = (int64_t)1 << 28;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
@@ -229,7 +233,7 @@ int fp8_weight_stream_layout(const uint8_t* wq, int64_t N, int64_t K, uint8_t* w
 int fp8_gemm_fwd_stream(const uint8_t* xq, const float* xs, const uint8_t* wq_s, const float* ws, void* y,
                         int64_t M, int64_t N, int64_t K, void* stream) {
   const fp8bsq_gemm_problem pr{xq, xs, wq_s, ws, y, M, N, K};
-  if (M > kStreamMaxTokens) return FP8BSQ_ERR_SHAPE;
+  if (M > kStreamMaxTokens || N >= kStreamMaxRows) return FP8BSQ_ERR_SHAPE;
   const int st = check_problem(Role::Fwd, pr);
   if (st != kLaunch) return st;
   return hip_status(fp8bsq::launch_gemm_fwd_stream(xq, xs, wq_s, ws, y, M, N, K, as_stream(stream)));

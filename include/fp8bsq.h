@@ -311,7 +311,8 @@ int fp8_weight_stream_layout(const uint8_t* wq, int64_t N, int64_t K, uint8_t* w
  *   y  out: bf16 [M, N], bit-identical to fp8_gemm_fwd(xq, xs, wq, ws, y, M, N, K)
  * For decode the GEMM is bound by reading the weight once; the stream layout
  * lets each wavefront read its weight rows as one sequential stream.
- * Shape: 1 <= M <= 64 (M = 0 is a no-op), N % 8 == 0, K % 8 == 0, Kp < 2^24.
+ * Shape: 1 <= M <= 64 (M = 0 is a no-op), N % 8 == 0, N < 2^28, K % 8 == 0,
+ * Kp < 2^24.
  */
 int fp8_gemm_fwd_stream(const uint8_t* xq, const float* xs, const uint8_t* wq_s, const float* ws, void* y,
                         int64_t M, int64_t N, int64_t K, void* stream);

@@ -205,3 +205,5 @@ def test_stream_layout_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, MISALIGNED, 1, 128, 128, None) == 3
     assert f(None, None, None, None, None, 0, 128, 128, None) == 0     # M == 0: no-op
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 128, 0, None) == 2       # empty contraction
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1 << 28, 128, None) == 2  # weight rows < 2^28 (launch size)
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 1, (1 << 28) - 8, 128, None) == 1
