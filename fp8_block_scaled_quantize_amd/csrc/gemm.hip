@@ -257,12 +257,16 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
     ccarry[b] = 0.0f;
   }
   f32x4 rprev = zero;
-  // The loop body is instantiated twice: with 8 wavefronts, the second
-  // wavefront of each SIMD (waves 4-7) issues its copies one slice later than
-  // the first, so the two do not stall on copy issue at the same moments
-  // (+4 % on WGrad, neutral elsewhere). The offset is a compile-time
-  // constant so the unrolled slices stay free of branches.
-  constexpr int LOAD_SLICES_ = (P_INSTR % 4 == 0 && Q_INSTR % 4 == 0) ? 4 : 2;   // slices over which a step's copies are spread
+  // A step's copies go out over two slices. The loop body is instantiated
+  // twice: with 8 wavefronts, the second wavefront of each SIMD (waves 4-7)
+  // issues its copies one slice later than the first (two for WGrad, whose
+  // slices carry twice the promotion VALU), so the two do not stall on copy
+  // issue at the same moments. Against four slices and a one-slice offset
+  // for every role (outputs identical): the grouped WGrad of the 32B linears
+  // at 32768 tokens 2-3 % faster, their forward and DGrad 0.2-1.1 %, the
+  // 4096-token GEMMs up to 5 %. The offset is a compile-time constant so the
+  // unrolled slices stay free of branches.
+  constexpr int LOAD_SLICES_ = 2;   // slices over which a step's copies are spread
   auto main_loop = [&](auto copy_offset) {
   constexpr int OFF = decltype(copy_offset)::value;
   int st = 0;                       // stage of step kb
@@ -358,7 +362,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
     st = st + 1 == NST ? 0 : st + 1;
   }
   };
-  constexpr int OFF_HI = (C::NT == 512 && SI >= LOAD_SLICES_ + 1) ? 1 : 0;
+  constexpr int OFF_HI = C::NT != 512 ? 0 : (PS_ROW && SI >= LOAD_SLICES_ + 2) ? 2 : (SI >= LOAD_SLICES_ + 1) ? 1 : 0;
   if (OFF_HI && wave >= 4)
     main_loop(std::integral_constant<int, OFF_HI>{});
   else
