@@ -259,13 +259,14 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
   f32x4 rprev = zero;
   // A step's copies go out over two slices. The loop body is instantiated
   // twice: with 8 wavefronts, the second wavefront of each SIMD (waves 4-7)
-  // issues its copies one slice later than the first (two for WGrad, whose
-  // slices carry twice the promotion VALU), so the two do not stall on copy
-  // issue at the same moments. Against four slices and a one-slice offset
-  // for every role (outputs identical): the grouped WGrad of the 32B linears
-  // at 32768 tokens 2-3 % faster, their forward and DGrad 0.2-1.1 %, the
-  // 4096-token GEMMs up to 5 %. The offset is a compile-time constant so the
-  // unrolled slices stay free of branches.
+  // may issue its copies later than the first, so the two do not stall on
+  // copy issue at the same moments: two slices later in WGrad (whose slices
+  // carry twice the promotion VALU), one in the medium tile's forward and
+  // DGrad, none in the large tile's. Against four slices and a one-slice
+  // offset for every role (outputs identical): the grouped WGrad of the 32B
+  // linears at 32768 tokens 2-3 % faster, their forward and DGrad 1-2 %. The
+  // offset is a compile-time constant so the unrolled slices stay free of
+  // branches.
   constexpr int LOAD_SLICES_ = 2;   // slices over which a step's copies are spread
   auto main_loop = [&](auto copy_offset) {
   constexpr int OFF = decltype(copy_offset)::value;
@@ -362,7 +363,11 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
     st = st + 1 == NST ? 0 : st + 1;
   }
   };
-  constexpr int OFF_HI = C::NT != 512 ? 0 : (PS_ROW && SI >= LOAD_SLICES_ + 2) ? 2 : (SI >= LOAD_SLICES_ + 1) ? 1 : 0;
+  constexpr int OFF_HI = C::NT != 512                        ? 0
+                         : (PS_ROW && SI >= LOAD_SLICES_ + 2) ? 2
+                         : C::BJ == 256                       ? 0
+                         : (SI >= LOAD_SLICES_ + 1)           ? 1
+                                                              : 0;
   if (OFF_HI && wave >= 4)
     main_loop(std::integral_constant<int, OFF_HI>{});
   else
