@@ -336,13 +336,16 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
           promote1(acc[SI - 1][b], dprev[b], ccarry[b], rprev);
         dprev[b] = dcur;
       }
-      // one MFMA, then the promotion of the partial it replaced, in turn
-      // (the row-scaled role schedules better left to the compiler)
+      // MFMAs, then the promotions of the partials they replaced, in turn:
+      // two at a time on the large tile (1-2 % faster there than one at a
+      // time, 1-3 % slower on the medium tile), one at a time otherwise (the
+      // row-scaled role schedules better left to the compiler)
       if (!PS_ROW) {
+        constexpr int SG = C::BJ == 256 ? 2 : 1;
 #pragma unroll
-        for (int b = 0; b < SJ; ++b) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, PROMOTE_VALU, 0);
+        for (int b = 0; b < SJ; b += SG) {
+          __builtin_amdgcn_sched_group_barrier(0x008, SG, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, SG * PROMOTE_VALU, 0);
         }
       }
       rprev = rs;
