@@ -342,6 +342,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
       // row-scaled role schedules better left to the compiler)
       if (!PS_ROW) {
         constexpr int SG = C::BJ == 256 ? 2 : 1;
+        static_assert(SJ % SG == 0, "schedule groups of SG column slices");
 #pragma unroll
         for (int b = 0; b < SJ; b += SG) {
           __builtin_amdgcn_sched_group_barrier(0x008, SG, 0);
