@@ -89,7 +89,9 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((ch
 // One workgroup's output tile: tile number `bid` of the `nblk` tiles of
 // problem p (a plain launch passes its block index and grid size; a grouped
 // launch its block's offset within the problem).
-template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
+// V4: K/128 is a multiple of 4 (for every problem of a grouped launch), so
+// each row's scales for 4 consecutive K steps are one aligned 16-byte copy.
+template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP, bool V4>
 __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses LDS address-space casts, device pass only
   using C = GemmCfg<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST>;
@@ -172,12 +174,17 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
     dma4(pf_base + kb * 128, pf_off, (uint32_t)__builtin_amdgcn_readfirstlane((int)(sink_lds + wave * 256)));
   };
 
-  // ---- scales. Thread t < ROWSC owns row t of the per-row scales (Q rows,
-  //      then for WGrad the P rows) and fetches 4 consecutive K steps of it
-  //      at once (one 16-byte copy when K/128 is a multiple of 4), a group
-  //      ahead. The last wavefront's first lanes fetch the block P scales
-  //      each K step. ----
-  const bool vec4 = (p.Kb & 3) == 0;
+  // ---- scales. The per-row scales (Q rows, then for WGrad the P rows) go to
+  //      LDS as [row][4]: 4 consecutive K steps of each row, a group of 4
+  //      steps ahead. When K/128 is a multiple of 4, lane t < ROWSC fetches
+  //      row t's group with one 16-byte copy; otherwise a row's group is not
+  //      16-byte aligned, and four 4-byte copies per wavefront fill the same
+  //      layout, lane L taking step L % 4 of row L / 4 of each quarter of the
+  //      wavefront's 64 rows (steps past the last repeat it and are never
+  //      read). Both are LDS DMA copies, waited for with the operand copies
+  //      (plain loads here made the wavefront wait for them, and with them
+  //      for every copy in flight, once per group: 7-10 % slower). The last
+  //      wavefront's first lanes fetch the block P scales each K step. ----
   auto load_row_scales = [&](int grp) {   // K steps 4grp .. 4grp+3 into rowsc[grp & 1]
 #pragma unroll
     for (int pass = 0; pass < C::ROW_PASSES; ++pass) {
@@ -186,14 +193,39 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
       if (rw >= C::ROWSC) continue;
       const bool q_rows = rw < C::BJ;                     // the 64 rows are all Q or all P rows
       const float* rbase = q_rows ? p.Qs + (int64_t)j0 * p.Kb : p.Ps + (int64_t)i0 * p.Kb;
-      const int rrow = q_rows ? min(r, qrows - 1) : min(r - C::BJ, prows - 1);
       const int k0 = 4 * grp;
-      if (vec4) {
-        dma16(rbase, (uint32_t)((rrow * p.Kb + k0) * 4), rowsc_lds + ((grp & 1) * C::ROWSC + rw) * 16);
-      } else {
-        const float* src = rbase + (int64_t)rrow * p.Kb;
+      const uint32_t dst = rowsc_lds + ((grp & 1) * C::ROWSC + rw) * 16;
+      if (V4) {
+        // Launches of this form always have K/128 a multiple of 4; the
+        // runtime test and the plain stores behind it are never taken, but
+        // without them the compiler allocates the large row-scaled tile
+        // differently and the grouped WGrad ran 2-2.5 % slower (same bits).
+        const int rrow = q_rows ? min(r, qrows - 1) : min(r - C::BJ, prows - 1);
+        if ((p.Kb & 3) == 0) {
+          dma16(rbase, (uint32_t)((rrow * p.Kb + k0) * 4), dst);
+        } else {
+          const float* src = rbase + (int64_t)rrow * p.Kb;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) rowsc[grp & 1][r * 4 + q] = k0 + q < p.Kb ? src[k0 + q] : 0.0f;
+          for (int q = 0; q < 4; ++q) rowsc[grp & 1][r * 4 + q] = k0 + q < p.Kb ? src[k0 + q] : 0.0f;
+        }
+      } else {
+        // (the lane index passes through an empty asm so that the offsets are
+        // computed here, once per group, instead of held in registers across
+        // the K loop, where the large tile has none to spare)
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        const int kq = min(k0 + (l & 3), p.Kb - 1);
+        const int r0 = (q_rows ? rw : rw - C::BJ) + (l >> 2);      // Q or P row of quarter 0
+        const int rmax = (q_rows ? qrows : prows) - 1;
+#pragma unroll
+        for (int qtr = 0; qtr < 4; ++qtr) {
+          // Without CLAMP every configuration runs only on whole tiles, so all
+          // 64 rows exist and the quarter moves the scalar base, not the lane offset.
+          if (CLAMP)
+            dma4(rbase, (uint32_t)((min(r0 + 16 * qtr, rmax) * p.Kb + kq) * 4), dst + qtr * 256);
+          else
+            dma4(rbase + (int64_t)(16 * qtr) * p.Kb, (uint32_t)((r0 * p.Kb + kq) * 4), dst + qtr * 256);
+        }
       }
     }
   };
@@ -449,7 +481,7 @@ __device__ __forceinline__ void gemm_body(const GemmParams& p, int bid, int nblk
 
 template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
 __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_kernel(GemmParams p) {
-  gemm_body<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP>(p, (int)blockIdx.x, (int)gridDim.x);
+  gemm_body<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP, true>(p, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // Several problems of one role in one launch: problem g owns the blocks
@@ -471,15 +503,65 @@ __global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_grouped_kerne
   const int nblk = p.tiles_i * p.tiles_j;
   const int local = bid - gp.start[g];
   if (local >= nblk) return;
-  gemm_body<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP>(p, local, nblk);
+  gemm_body<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP, true>(p, local, nblk);
+}
+// The same where some problem's K/128 is not a multiple of 4 (plain calls
+// of such a K go out as a group of one): a kernel of its own, so that the
+// other form of the scale copies costs the common one no registers (in the
+// plain kernel it made the large tile spill). (Both are written out in full:
+// the grouped WGrad measured 4 % slower with their common part in a shared
+// inline function, whose extra level changed the register allocation.)
+template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
+__global__ __launch_bounds__(64 * WAVES_I * WAVES_J) void fp8_gemm_grouped_kernel_unaligned(GroupedParams gp) {
+  const int bid = (int)blockIdx.x;
+  const int g = grouped_problem(bid, gp.start, gp.count);   // uniform over the workgroup
+  const GemmParams& p = gp.prob[g];
+  const int nblk = p.tiles_i * p.tiles_j;
+  const int local = bid - gp.start[g];
+  if (local >= nblk) return;
+  gemm_body<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP, false>(p, local, nblk);
 }
 
 // ----------------------------------------------------------------------------
 // Launch one tile configuration.
 // ----------------------------------------------------------------------------
 template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
+static hipError_t run_grouped_cfg(const GemmParams* probs, int count, hipStream_t stream) {
+  using C = GemmCfg<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST>;
+  GroupedParams gp{};
+  gp.count = count;
+  // Each problem's block range starts at a multiple of the XCD count; with
+  // 8 wavefronts (one workgroup per compute unit) at a multiple of 256, so
+  // that a problem's chip-wide 16 x 16 supertiles line up with the rounds of
+  // 256 workgroups the chip runs at once (grouped WGrad of the 32B linears at
+  // 32768 tokens: 12.07 -> 11.99 ms; the padding blocks exit at once).
+  constexpr int ALIGN = C::NT == 512 ? 256 : NUM_XCD;
+  int tiles[kMaxGroup];
+  bool v4 = true;
+  for (int g = 0; g < count; ++g) {
+    GemmParams q = probs[g];
+    v4 = v4 && (q.Kb & 3) == 0;
+    q.tiles_i = (q.I + C::BI - 1) / C::BI;
+    q.tiles_j = (q.J + C::BJ - 1) / C::BJ;
+    gp.prob[g] = q;
+    tiles[g] = q.tiles_i * q.tiles_j;
+  }
+  const int total = grouped_layout(tiles, count, ALIGN, gp.start);
+  if (v4)
+    hipLaunchKernelGGL((fp8_gemm_grouped_kernel<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP>), dim3(total),
+                       dim3(C::NT), 0, stream, gp);
+  else
+    hipLaunchKernelGGL((fp8_gemm_grouped_kernel_unaligned<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP>),
+                       dim3(total), dim3(C::NT), 0, stream, gp);
+  return hipGetLastError();
+}
+
+template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
 static hipError_t run_gemm_cfg(GemmParams p, hipStream_t stream) {
   using C = GemmCfg<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST>;
+  // a K/128 that is not a multiple of 4: the grouped kernel with that form of
+  // the scale copies, one problem (same tiles, same order, same bits)
+  if ((p.Kb & 3) != 0) return run_grouped_cfg<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP>(&p, 1, stream);
   p.tiles_i = (p.I + C::BI - 1) / C::BI;
   p.tiles_j = (p.J + C::BJ - 1) / C::BJ;
   const int nblk = p.tiles_i * p.tiles_j;
@@ -542,31 +624,6 @@ static hipError_t run_gemm(GemmParams p, hipStream_t stream) {
   if (p.I >= 128 && p.J >= 64 && small_tiles >= 512) return run_gemm_cfg<2, 2, 4, 2, PS_ROW, 3, false>(p, stream);
   if (p.I >= 64 && p.J >= 64) return run_gemm_cfg<2, 2, 2, 2, PS_ROW, 4, false>(p, stream);
   return run_gemm_cfg<2, 2, 2, 2, PS_ROW, 4, true>(p, stream);
-}
-
-template <int WAVES_I, int WAVES_J, int SI, int SJ, bool PS_ROW, int NST, bool CLAMP>
-static hipError_t run_grouped_cfg(const GemmParams* probs, int count, hipStream_t stream) {
-  using C = GemmCfg<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST>;
-  GroupedParams gp{};
-  gp.count = count;
-  // Each problem's block range starts at a multiple of the XCD count; with
-  // 8 wavefronts (one workgroup per compute unit) at a multiple of 256, so
-  // that a problem's chip-wide 16 x 16 supertiles line up with the rounds of
-  // 256 workgroups the chip runs at once (grouped WGrad of the 32B linears at
-  // 32768 tokens: 12.07 -> 11.99 ms; the padding blocks exit at once).
-  constexpr int ALIGN = C::NT == 512 ? 256 : NUM_XCD;
-  int tiles[kMaxGroup];
-  for (int g = 0; g < count; ++g) {
-    GemmParams q = probs[g];
-    q.tiles_i = (q.I + C::BI - 1) / C::BI;
-    q.tiles_j = (q.J + C::BJ - 1) / C::BJ;
-    gp.prob[g] = q;
-    tiles[g] = q.tiles_i * q.tiles_j;
-  }
-  const int total = grouped_layout(tiles, count, ALIGN, gp.start);
-  hipLaunchKernelGGL((fp8_gemm_grouped_kernel<WAVES_I, WAVES_J, SI, SJ, PS_ROW, NST, CLAMP>), dim3(total),
-                     dim3(C::NT), 0, stream, gp);
-  return hipGetLastError();
 }
 
 // One configuration for the whole group: the large one when every problem

@@ -294,6 +294,62 @@ def test_grouped_equals_plain_calls(role, shapes):
         assert torch.equal(o, r), f"{role} problem {i}"
 
 
+# ----------------------------------- K / 128 not a multiple of 4 (any K) --
+#
+# The per-row scales of 4 consecutive K blocks reach LDS with one 16-byte copy
+# per row when the contraction has a multiple of 4 blocks, and with 4-byte
+# copies (a kernel of its own) otherwise. Padding the contraction with +0
+# codes up to the next multiple of 4 blocks (scale 1 there) only adds exact
+# zeros to every running sum, so the two forms must give the same bits; the
+# plain form is checked against the oracle everywhere else.
+
+def _pad_contraction(role, ops, kb_to):
+    """The same problem with its contraction padded by +0 codes to kb_to blocks."""
+    def pad_codes(t):            # contraction along dim 1
+        out = torch.zeros(t.shape[0], 128 * kb_to, dtype=t.dtype, device=t.device)
+        out[:, :t.shape[1]] = t
+        return out
+
+    def pad_cols(s):             # scales with the contraction along dim 1
+        out = torch.ones(s.shape[0], kb_to, dtype=s.dtype, device=s.device)
+        out[:, :s.shape[1]] = s
+        return out
+
+    def pad_rows(s):             # block scales with the contraction along dim 0
+        out = torch.ones(kb_to, s.shape[1], dtype=s.dtype, device=s.device)
+        out[:s.shape[0]] = s
+        return out
+
+    a, sa, b, sb = ops
+    if role == "fwd":
+        return pad_codes(a), pad_cols(sa), pad_codes(b), pad_cols(sb)
+    if role == "dgrad":
+        return pad_codes(a), pad_cols(sa), pad_codes(b), pad_rows(sb)
+    return pad_codes(a), pad_cols(sa), pad_codes(b), pad_cols(sb)
+
+
+@pytest.mark.parametrize("role", ["fwd", "dgrad", "wgrad"])
+@pytest.mark.parametrize("rows,cols,kb", [
+    (4096, 4096, 3),      # large tiles, one partial group
+    (4096, 4096, 9),      # large tiles, two whole groups and a partial one
+    (4096, 4096, 65),     # large tiles, long contraction (chip-wide tile order)
+    (4096, 2048, 6),      # small tiles
+    (200, 640, 5),        # tiny tiles, a ragged dimension
+    (40, 128, 2),         # clamped tiny tiles
+])
+def test_any_k_block_count_equals_zero_padded(role, rows, cols, kb):
+    kb_to = (kb + 3) // 4 * 4
+    L = 128 * kb
+    M, N, K = {"fwd": (rows, cols, L), "dgrad": (rows, L, cols), "wgrad": (L, rows, cols)}[role]
+    note(f"{role} with {kb} K blocks vs zero-padded to {kb_to}: M={M} N={N} K={K}")
+    ops = _quantized_problem(role, M, N, K, seed=1000 + kb)
+    plain = getattr(fq, f"fp8_gemm_{role}")
+    out = plain(*ops)
+    padded = plain(*_pad_contraction(role, ops, kb_to))
+    torch.cuda.synchronize()
+    assert torch.equal(out, padded), f"{role} {kb} K blocks: differs from the zero-padded contraction"
+
+
 # ------------------------------------------- oracle operands, small shapes --
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (17, 384, 256), (300, 640, 1152), (64, 256, 4096)])
